@@ -1,0 +1,176 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies an oracle source file, plants one plausible mistake (a dropped
+term, a wrong index or sign, a transposed operand, an off-by-one), loads the
+copy as a throwaway module and runs a compact version of the pins against it.
+At least one pin must reject every mutant; the unmutated source must pass all
+of them.  Nothing here touches the real oracle modules.
+"""
+
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+RNG = np.random.default_rng(99)
+
+
+def _load(fname, old=None, new=None, extra=None):
+    path = os.path.join(ROOT, "oracle", fname)
+    src = open(path).read()
+    if old is not None:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new, 1)
+    src = src.replace("from .attention import attention_forward", "")
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__.update(extra or {})
+    exec(compile(src, path, "exec"), mod.__dict__)
+    return mod
+
+
+def _golden(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- attention pins
+
+def _attention_pins_pass(mod):
+    f = mod.attention_forward
+    try:
+        for c in _golden("attention_worked_examples.json")["cases"]:
+            o, lse = f(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]), scale=c["scale"], causal=c["causal"])
+            if not (np.allclose(o, c["o"], atol=1e-12, rtol=0) and np.allclose(lse, c["lse"], atol=1e-12, rtol=0)):
+                return False
+        for causal in (False, True):
+            q, k, v = RNG.standard_normal((1, 9, 4, 5)), RNG.standard_normal((1, 9, 2, 5)), RNG.standard_normal((1, 9, 2, 3))
+            o, _ = f(q, k, v, scale=0.5, causal=causal)
+            t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                t(q), t(k), t(v), is_causal=causal, scale=0.5, enable_gqa=True).permute(0, 2, 1, 3).numpy()
+            if not np.allclose(o, ref, atol=1e-12, rtol=0):
+                return False
+            o0, lse0 = f(np.zeros((1, 7, 1, 5)), k[:, :7, :1], v[:, :7, :1], scale=1.0, causal=causal)
+            n = np.arange(1, 8) if causal else np.full(7, 7)
+            if not np.allclose(lse0[0, 0], np.log(n), atol=1e-14, rtol=0):
+                return False
+    except Exception:
+        return False
+    return True
+
+
+ATTENTION_MUTANTS = [
+    ("gqa_modulo", "g = h // group", "g = h % hk"),
+    ("dropped_scale", "s = scale * (qh @ kg.T)", "s = (qh @ kg.T)"),
+    ("causal_off_by_one", "key_idx[None, :] <= rows_arr[:, None]", "key_idx[None, :] < rows_arr[:, None] + 0 * 1"),
+    ("causal_transposed", "key_idx[None, :] <= rows_arr[:, None]", "key_idx[None, :] >= rows_arr[:, None]"),
+    ("lse_drops_max", "m_safe + np.log(", "0.0 + np.log("),
+    ("sum_wrong_axis", "l = p.sum(axis=1)", "l = p.sum(axis=0)"),
+    ("transposed_pv", "out = (p @ vg)", "out = (p.T @ vg)"),
+    ("sign_of_max", "p = np.exp(s - m_safe[:, None])", "p = np.exp(s + m_safe[:, None])"),
+]
+
+
+def test_attention_source_passes_pins():
+    assert _attention_pins_pass(_load("attention.py"))
+
+
+@pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
+def test_attention_mutant_is_caught(name, old, new):
+    assert not _attention_pins_pass(_load("attention.py", old, new))
+
+
+# ---------------------------------------------------------------- gate pins
+
+def _gate_pins_pass(mod):
+    try:
+        for c in _golden("gate_worked_examples.json")["cases"]:
+            r = mod.k_smooth_mean(np.array(c["k"]), key_stride=c["key_stride"], max_keys=c["max_keys"], tau=c["tau"])
+            ratio = np.array([[math.inf if x == "inf" else float(x) for x in row] for row in c["ratio"]])
+            if not (np.allclose(r["mu"], c["mu"], atol=1e-15) and np.allclose(r["var"], c["var"], atol=1e-15)
+                    and np.array_equal(r["ratio"], ratio) and np.array_equal(r["open"], c["open"])
+                    and np.array_equal(r["mean"], c["mean"])):
+                return False
+        if list(mod.key_sample(10, 3)) != [0, 3, 6, 9]:
+            return False
+    except Exception:
+        return False
+    return True
+
+
+GATE_MUTANTS = [
+    ("uncentred_variance", "((x - mu[:, None, :, :]) ** 2)", "(x ** 2)"),
+    ("threshold_inclusive", "gate_open = ratio > tau", "gate_open = ratio >= tau"),
+    ("sample_count_floor", "count = (sk + key_stride - 1) // key_stride", "count = sk // key_stride"),
+    ("closed_keeps_mean", "mean = np.where(gate_open[:, :, None], mu, 0.0)", "mean = mu"),
+    ("ratio_not_rooted", "ratio[bi, g] = math.sqrt(num[bi, g] / den[bi, g])", "ratio[bi, g] = num[bi, g] / den[bi, g]"),
+]
+
+
+def test_gate_source_passes_pins():
+    assert _gate_pins_pass(_load("gate.py"))
+
+
+@pytest.mark.parametrize("name,old,new", GATE_MUTANTS, ids=[m[0] for m in GATE_MUTANTS])
+def test_gate_mutant_is_caught(name, old, new):
+    assert not _gate_pins_pass(_load("gate.py", old, new))
+
+
+# ---------------------------------------------------------------- fp8 pins
+
+def _fp8_pins_pass(mod):
+    try:
+        g = _golden("e4m3_ocp_codes.json")
+        for c in g["codes"]:
+            if mod.e4m3_decode(np.uint8(int(c["code"], 16))) != c["value"]:
+                return False
+            if int(mod.e4m3_encode(np.float64(c["value"]))) != int(c["code"], 16):
+                return False
+        for c in g["rounding"]["cases"]:
+            if mod.e4m3_round(np.float64(c["x"])) != c["rounded"]:
+                return False
+        x = (RNG.standard_normal(20000) * 30).astype(np.float32)
+        x = x[np.abs(x) < 464]
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        if not np.array_equal(mod.e4m3_round(x), ref):
+            return False
+        xb = (RNG.standard_normal((1, 200, 1, 8)) * 3).astype(np.float32)
+        codes, scales, _ = mod.quantize_blocks(xb)
+        if scales.shape != (1, 1, 2) or scales[0, 0, 0] != np.float32(np.abs(xb[0, :128]).max() / np.float32(448)):
+            return False
+        k = np.ones((1, 4, 1, 2), dtype=np.float32) * 3.0
+        mu = np.full((1, 1, 2), 1.0, dtype=np.float32)
+        if not np.array_equal(mod.smooth_k(k, mu), np.full((1, 4, 1, 2), 2.0, dtype=np.float32)):
+            return False
+    except Exception:
+        return False
+    return True
+
+
+def _fp8_extra():
+    from oracle.attention import attention_forward
+    return {"attention_forward": attention_forward}
+
+
+FP8_MUTANTS = [
+    ("truncate_not_round", "r = np.rint(mag / quantum) * quantum", "r = np.floor(mag / quantum) * quantum"),
+    ("no_subnormals", "e = np.maximum(e, E4M3_MIN_NORMAL_EXP)", "e = e"),
+    ("fnuz_max", "E4M3_MAX = 448.0", "E4M3_MAX = 240.0"),
+    ("smoothing_sign", "(k32 - mu32[:, None, :, :])", "(k32 + mu32[:, None, :, :])"),
+    ("block_64", "BLOCK_TOKENS = 128", "BLOCK_TOKENS = 64"),
+    ("bias_8", "E4M3_BIAS = 7", "E4M3_BIAS = 8"),
+]
+
+
+def test_fp8_source_passes_pins():
+    assert _fp8_pins_pass(_load("fp8.py", extra=_fp8_extra()))
+
+
+@pytest.mark.parametrize("name,old,new", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
+def test_fp8_mutant_is_caught(name, old, new):
+    assert not _fp8_pins_pass(_load("fp8.py", old, new, extra=_fp8_extra()))

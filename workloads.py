@@ -1,0 +1,113 @@
+"""Seeded synthetic workloads shared by the tests, the bench and the smoke check.
+
+This module only draws random numbers and names shapes. It holds none of the
+attention, gate or quantisation arithmetic: the HIP library and the CPU oracle
+each implement those on their own, and both receive the same input bits from
+here.
+
+Shapes follow the attention-forward workloads the pages time (the Triton MHA
+forward retune page, "Test Plan" smoke commands and "Profile 1"/"Profile 2";
+the mha_v4 K-smoothing gate page, "Performance" table).  The pages' own shape
+lists (model_shapes.json and friends) are not available, so these seeded
+N(0, 1) tensors stand in for them.
+
+Recipe: a CPU ``torch.Generator`` seeded per workload draws float32 ``randn``
+in BSHD order Q, then K, then V (then, for the FP8 workload, a per-head,
+per-channel K bias ~ N(0, 3^2) of shape [h, d]); each tensor is rounded to
+bfloat16 (round-to-nearest-even).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    b: int
+    hq: int
+    hk: int
+    sq: int
+    sk: int
+    d_qk: int
+    d_v: int
+    causal: bool
+    seed: int
+    fp8: bool = False
+    k_bias_std: float = 0.0  # per-(head, channel) K bias, FP8 smoothing workload only
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+    def flops(self) -> float:
+        """Algorithmic attention FLOPs: 2*b*hq*sq*sk*(d_qk + d_v), halved when causal."""
+        f = 2.0 * self.b * self.hq * self.sq * self.sk * (self.d_qk + self.d_v)
+        return f / 2.0 if self.causal else f
+
+
+WORKLOADS = {
+    "tiny_d64": Workload(
+        "tiny_d64", b=1, hq=2, hk=2, sq=128, sk=128, d_qk=64, d_v=64, causal=False, seed=101,
+        description="b1 hq2 hk2 128^2 d64 non-causal bf16"),
+    "gqa_d64_causal": Workload(
+        "gqa_d64_causal", b=8, hq=48, hk=8, sq=2048, sk=2048, d_qk=64, d_v=64, causal=True, seed=102,
+        description="b8 hq48 hk8 2048^2 d64 causal bf16"),
+    "gqa_d128_causal": Workload(
+        "gqa_d128_causal", b=1, hq=32, hk=8, sq=4096, sk=4096, d_qk=128, d_v=128, causal=True, seed=103,
+        description="b1 hq32 hk8 4096^2 d128 causal bf16"),
+    "mla_d192_d128_causal": Workload(
+        "mla_d192_d128_causal", b=1, hq=128, hk=128, sq=8192, sk=8192, d_qk=192, d_v=128, causal=True,
+        seed=104, description="b1 hq128 hk128 8192^2 dqk192 dv128 causal bf16"),
+    "fp8_ksmooth_d128": Workload(
+        "fp8_ksmooth_d128", b=1, hq=16, hk=16, sq=4096, sk=4096, d_qk=128, d_v=128, causal=False,
+        seed=105, fp8=True, k_bias_std=3.0,
+        description="b1 h16 4096^2 d128 non-causal, bf16 in, K smoothed, e4m3 compute, bf16 out"),
+}
+
+
+def _randn(gen: torch.Generator, shape) -> torch.Tensor:
+    """float32 N(0,1) drawn in row-major order, then rounded to bfloat16."""
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_qkv(w: Workload, seed: Optional[int] = None, k_bias_std: Optional[float] = None):
+    """Return (q, k, v) bfloat16 CPU tensors in BSHD layout for workload ``w``.
+
+    ``k_bias_std`` overrides the workload's K bias (0 gives plain N(0,1) K).
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    q = _randn(gen, (w.b, w.sq, w.hq, w.d_qk))
+    k32 = torch.randn((w.b, w.sk, w.hk, w.d_qk), generator=gen, dtype=torch.float32)
+    v = _randn(gen, (w.b, w.sk, w.hk, w.d_v))
+    std = w.k_bias_std if k_bias_std is None else k_bias_std
+    if std != 0.0:
+        bias = torch.randn((w.hk, w.d_qk), generator=gen, dtype=torch.float32) * std
+        k32 = k32 + bias.view(1, 1, w.hk, w.d_qk)
+    k = k32.to(torch.bfloat16)
+    return q, k, v
+
+
+def make_random(shape, seed: int, dtype=torch.bfloat16, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:
+    """A seeded N(mean, std^2) tensor of ``shape`` (drawn in float32, then cast)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    x = torch.randn(shape, generator=gen, dtype=torch.float32) * std + mean
+    return x.to(dtype)
+
+
+def sample_indices(n: int, count: int, seed: int, include=()) -> list:
+    """A sorted, seeded subset of range(n) of about ``count`` items, plus ``include``."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    count = min(count, n)
+    picked = set(int(i) for i in torch.randperm(n, generator=gen)[:count])
+    picked.update(int(i) % n for i in include if n > 0)
+    return sorted(picked)

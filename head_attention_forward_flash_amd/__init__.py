@@ -1,0 +1,196 @@
+"""Python binding of libmha, the gfx950 fused attention forward library.
+
+Thin ctypes marshalling over the C ABI in include/mha.h: every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device memory
+and the current stream only.  There is no fallback: if libmha.so is missing or
+the tensors are not on a ROCm device the calls raise.
+
+Entry points (same names as the C ABI):
+    mha_fwd_bf16(q, k, v, causal=False, softmax_scale=None, out=None, lse=True)
+    k_smooth_mean(k, key_stride=1, max_keys=0, tau=0.25)
+    mha_fwd_fp8(q, k, v, k_mean=None, causal=False, softmax_scale=None, out=None, lse=True)
+Tensors are BSHD views with a contiguous channel dimension.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
+
+MHA_OK = 0
+STATUS_NAMES = {
+    0: "MHA_OK", 1: "MHA_ERR_NULL", 2: "MHA_ERR_SHAPE", 3: "MHA_ERR_UNSUPPORTED", 4: "MHA_ERR_LAYOUT",
+    5: "MHA_ERR_OVERFLOW", 6: "MHA_ERR_WORKSPACE", 7: "MHA_ERR_HIP", 8: "MHA_ERR_VALUE",
+}
+
+# Every symbol include/mha.h declares.
+EXPORTED_SYMBOLS = (
+    "mha_fwd_bf16", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
+    "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_status_string", "mha_last_error",
+)
+
+
+class MhaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmha.so and declare the C signatures (no GPU call happens here)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m head_attention_forward_flash_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mha_fwd_bf16.restype = i32
+    lib.mha_fwd_bf16.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
+                                 i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.k_smooth_mean_workspace_bytes.restype = sz
+    lib.k_smooth_mean_workspace_bytes.argtypes = [i32] * 6
+    lib.k_smooth_mean.restype = i32
+    lib.k_smooth_mean.argtypes = [vp, Strides, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.mha_fwd_fp8_workspace_bytes.restype = sz
+    lib.mha_fwd_fp8_workspace_bytes.argtypes = [i32] * 6
+    lib.mha_fp8_workspace_layout.restype = i32
+    lib.mha_fp8_workspace_layout.argtypes = [i32] * 6 + [ctypes.POINTER(sz)]
+    lib.mha_fwd_fp8.restype = i32
+    lib.mha_fwd_fp8.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, vp, Strides, vp,
+                                i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_status_string.argtypes = [i32]
+    lib.mha_last_error.restype = ctypes.c_char_p
+    lib.mha_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != MHA_OK:
+        msg = load_library().mha_last_error().decode()
+        raise MhaError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bshd_strides(t) -> Strides:
+    if t.dim() != 4:
+        raise ValueError(f"expected a 4-d BSHD tensor, got shape {tuple(t.shape)}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the channel dimension must be contiguous (stride 1)")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_device(*tensors):
+    torch = _torch()
+    for t in tensors:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("tensors must live on a ROCm device (torch 'cuda' device)")
+
+
+def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
+                 lse: bool = True):
+    """Fused attention forward in bf16. Returns (o, lse) with lse [b, hq, sq] fp32 (or None)."""
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, out)
+    b, sq, hq, d_qk = q.shape
+    _, sk, hk, _ = k.shape
+    d_v = v.shape[3]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((b, sq, hq, d_v), dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
+    _check(lib.mha_fwd_bf16(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
+                            _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
+                            float(softmax_scale), int(bool(causal)), _stream(q.device)))
+    return out, lse_t
+
+
+def k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride=1, max_keys=0) -> int:
+    return int(load_library().k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys))
+
+
+def k_smooth_mean(k, key_stride: int = 1, max_keys: int = 0, tau: float = 0.25, workspace=None):
+    """K-smoothing gate. Returns (mean [b, hk, d] fp32, gate [b, hk] int32)."""
+    torch = _torch()
+    lib = load_library()
+    _require_device(k)
+    if k.dtype != torch.bfloat16:
+        raise ValueError("k must be bfloat16")
+    b, sk, hk, d = k.shape
+    mean = torch.empty((b, hk, d), dtype=torch.float32, device=k.device)
+    gate = torch.empty((b, hk), dtype=torch.int32, device=k.device)
+    need = k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    _check(lib.k_smooth_mean(_ptr(k), _bshd_strides(k), b, hk, sk, d, key_stride, max_keys, float(tau),
+                             _ptr(mean), _ptr(gate), _ptr(workspace), workspace.numel(), _stream(k.device)))
+    return mean, gate
+
+
+def mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d) -> int:
+    return int(load_library().mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d))
+
+
+def mha_fp8_workspace_layout(b, hq, hk, sq, sk, d):
+    """Byte offsets of (q codes, k codes, v codes, q scales, k scales, v scales) in the fp8 workspace."""
+    lib = load_library()
+    arr = (ctypes.c_size_t * 6)()
+    _check(lib.mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, arr))
+    return [int(x) for x in arr]
+
+
+def mha_fwd_fp8(q, k, v, k_mean=None, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
+                lse: bool = True, workspace=None):
+    """K-smoothed FP8 attention forward. Returns (o, lse, workspace)."""
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, k_mean, out)
+    b, sq, hq, d = q.shape
+    _, sk, hk, _ = k.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, sq, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
+    need = mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if k_mean is not None and (k_mean.dtype != torch.float32 or not k_mean.is_contiguous()):
+        raise ValueError("k_mean must be a contiguous float32 [b, hk, d] tensor")
+    _check(lib.mha_fwd_fp8(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
+                           _ptr(k_mean), _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d,
+                           float(softmax_scale), int(bool(causal)), _ptr(workspace), workspace.numel(),
+                           _stream(q.device)))
+    return out, lse_t, workspace

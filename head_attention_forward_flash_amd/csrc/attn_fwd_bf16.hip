@@ -1,0 +1,283 @@
+// Fused attention forward, bf16 in / bf16 out, fp32 accumulation, for gfx950.
+//
+// Computes O = softmax(scale * Q K^T + causal mask) V and the natural-log LSE per
+// row: the MHA forward pass tuned on "Tune MHA config & small-head pipeline
+// pathology" (Motivation; Technical Details: head-dim buckets 64, 128 and the
+// dqk=192/dv=128 "pe" bucket; Profile 2: pipelining depth as the main lever).
+//
+// Work decomposition: one workgroup of 4 waves per (batch, query head, block of
+// 128 query rows); each wave owns 32 query rows.  The kernel computes the
+// TRANSPOSED scores S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that every lane
+// holds one query row (lane % 32) and 32 of its keys per 64-key tile: the row
+// max and row sum then stay in the lane except for one exchange with lane ^ 32,
+// and the probabilities P^T are already laid out as the B operand of
+// O^T = V^T P^T (the key order inside one 16-key MFMA step is permuted the same
+// way on both operands, which leaves the contraction unchanged).
+//
+//   Q      32 rows x d_qk per wave, loaded once into registers (B operand).
+//   K      64 x d_qk tile in LDS, row-major, rows padded by 16 bytes (A operand,
+//          one ds_read_b128 per MFMA, conflict-free across 8 consecutive rows).
+//   V      64 x d_v tile written TRANSPOSED into LDS (channel-major, keys
+//          contiguous) so the A operand of O^T = V^T P^T is two ds_read_b64.
+//   tiles  global -> registers for tile t+1 is issued before computing tile t
+//          (register double buffering); LDS holds one tile.
+//   causal key tiles past the block's last row are never loaded; masking is
+//          applied only on tiles that cross the diagonal or the ragged end.
+//   softmax online, in base 2 (scores pre-multiplied by scale*log2 e); the
+//          running max is only moved when a row's max grows by more than 8
+//          (a factor 256), which keeps O and l consistent and rescales rarely.
+//
+// Every global load goes through a buffer resource clamped to the (batch, head)
+// slice, so rows past sq / sk read as zero instead of faulting.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mha {
+namespace {
+
+constexpr int BM = 128;       // query rows per workgroup
+constexpr int BN = 64;        // keys per tile
+constexpr int NTHREADS = 256;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
+    constexpr int KROW = DQK + 8;             // K row in LDS, elements (16-byte pad)
+    constexpr int VROW = BN + 4;              // V^T row in LDS, elements (8-byte pad)
+    constexpr int KSTEPS = DQK / 16;          // MFMA k-steps for S^T
+    constexpr int KCHUNKS = DQK / 32;         // 16-byte K chunks per thread per tile
+    constexpr int VKEYS = DV / 32;            // keys per thread when staging V (4 or 2)
+    constexpr int VKGROUPS = BN / VKEYS;      // key groups per tile
+    constexpr int CBLK = DV / 32;             // 32-channel output blocks
+    static_assert(BN * DQK / 8 == KCHUNKS * NTHREADS, "K staging must cover the tile");
+    static_assert(VKGROUPS * (DV / 8) == NTHREADS, "V staging must cover the tile");
+
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KROW];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[DV * VROW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;     // query column of this lane in S^T / O^T
+    const int half = lane >> 5;    // which half of the wave
+
+    // ---- workgroup -> (batch, head, query block); consecutive logical ids stay on one XCD
+    const int nwg = gridDim.x;
+    const int nwg8 = nwg & ~7;
+    const int pid = blockIdx.x;
+    const int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
+    const int mrev = lid % p.n_mblocks;
+    const int bh = lid / p.n_mblocks;
+    const int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first
+    const int h = bh % p.hq;
+    const int bb = bh / p.hq;
+    const int g = h / p.group;
+
+    const char* qbase = static_cast<const char*>(p.q) + 2 * (bb * p.qv.sb + h * p.qv.sh);
+    const char* kbase = static_cast<const char*>(p.k) + 2 * (bb * p.kv.sb + g * p.kv.sh);
+    const char* vbase = static_cast<const char*>(p.v) + 2 * (bb * p.vv.sb + g * p.vv.sh);
+    const auto qrs = make_rsrc(qbase, p.qv.slice_bytes);
+    const auto krs = make_rsrc(kbase, p.kv.slice_bytes);
+    const auto vrs = make_rsrc(vbase, p.vv.slice_bytes);
+
+    const int wave_row0 = mblk * BM + wave * 32;
+    const int my_row = wave_row0 + col;
+
+    // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[my_row][kk*16 + half*8 .. +8]
+    bf16x8 qf[KSTEPS];
+    {
+        const uint32_t rowoff = my_row < p.sq ? static_cast<uint32_t>(my_row * p.qv.ss * 2) : kOutOfRange;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
+            qf[kk] = __builtin_bit_cast(bf16x8, buffer_load_b128(qrs, off));
+        }
+    }
+
+    const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    // ---- staging registers for one K/V tile
+    u32x4 kreg[KCHUNKS];
+    u32x4 vreg[VKEYS];
+    const int vkg = tid % VKGROUPS;   // key group (VKEYS consecutive keys)
+    const int vcg = tid / VKGROUPS;   // 8-channel group
+
+    auto load_tile = [&](int t) {
+        const int key0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < KCHUNKS; ++i) {
+            const int c = tid + NTHREADS * i;
+            const int row = c / (DQK / 8);
+            const int ch = c % (DQK / 8);
+            const int key = key0 + row;
+            const uint32_t off = key < p.sk ? static_cast<uint32_t>(key * p.kv.ss * 2 + ch * 16) : kOutOfRange;
+            kreg[i] = buffer_load_b128(krs, off);
+        }
+#pragma unroll
+        for (int i = 0; i < VKEYS; ++i) {
+            const int key = key0 + vkg * VKEYS + i;
+            const uint32_t off = key < p.sk ? static_cast<uint32_t>(key * p.vv.ss * 2 + vcg * 16) : kOutOfRange;
+            vreg[i] = buffer_load_b128(vrs, off);
+        }
+    };
+
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < KCHUNKS; ++i) {
+            const int c = tid + NTHREADS * i;
+            const int row = c / (DQK / 8);
+            const int ch = c % (DQK / 8);
+            *reinterpret_cast<u32x4*>(&k_lds[row * KROW + ch * 8]) = kreg[i];
+        }
+        // V^T: channel (vcg*8 + e) row receives keys vkg*VKEYS .. +VKEYS
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int dw = e >> 1;
+            const bool hi = e & 1;
+            uint32_t w[VKEYS / 2];
+#pragma unroll
+            for (int i = 0; i < VKEYS / 2; ++i) {
+                const uint32_t a = vreg[2 * i][dw];
+                const uint32_t c2 = vreg[2 * i + 1][dw];
+                w[i] = hi ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
+            }
+            uint16_t* dst = &v_lds[(vcg * 8 + e) * VROW + vkg * VKEYS];
+            if constexpr (VKEYS == 4) {
+                *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+            } else {
+                *reinterpret_cast<uint32_t*>(dst) = w[0];
+            }
+        }
+    };
+
+    f32x16 oacc[CBLK];
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
+    float m_run = kNegInf;   // running max (log2 units), same in lane and lane^32
+    float l_run = 0.f;       // this lane's partial row sum over its half of the keys
+
+    if (ntiles > 0) load_tile(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
+
+        // ---- S^T = K Q^T for two 32-key blocks
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            const uint16_t* krow = &k_lds[(kb * 32 + col) * KROW + half * 8];
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + kk * 16));
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- scale, mask, tile max
+        const int key0 = t * BN;
+        const bool need_mask = (key0 + BN > p.sk) || (CAUSAL && key0 + BN - 1 > wave_row0);
+        float mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                float x = s[kb][j] * p.scale_log2;
+                if (need_mask) {
+                    const int key = key0 + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+                    if (key >= p.sk || (CAUSAL && key > my_row)) x = kNegInf;
+                }
+                s[kb][j] = x;
+                mt = fmaxf(mt, x);
+            }
+        }
+        mt = fmaxf(mt, swap_halves(mt));
+
+        // ---- online softmax with lazy rescaling
+        const float m_new = fmaxf(m_run, mt);
+        if (__any(m_new > m_run + kRescaleThreshold)) {
+            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+
+        bf16x8 pf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = fast_exp2(s[ks >> 1][(ks & 1) * 8 + 2 * i] - m_use);
+                const float p1 = fast_exp2(s[ks >> 1][(ks & 1) * 8 + 2 * i + 1] - m_use);
+                l_run += p0 + p1;
+                w[i] = pack_bf16x2(p0, p1);
+            }
+            pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+            const uint16_t* vrow = &v_lds[(cb * 32 + col) * VROW + half * 4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: normalise, store O (bf16) and LSE
+    const float l_tot = l_run + swap_halves(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (my_row < p.sq) {
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + (bb * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss);
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int ch = cb * 32 + grp * 8 + half * 4;
+                const uint32_t w0 = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
+                const uint32_t w1 = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + ch) = u32x2{w0, w1};
+            }
+        }
+        if (p.lse != nullptr && half == 0) {
+            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+            p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
+        }
+    }
+}
+
+template <int DQK, int DV, bool CAUSAL>
+hipError_t launch(const AttnParams& p, hipStream_t stream) {
+    const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(NTHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_fwd_bf16_block_m() { return BM; }
+
+hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
+    if (d_qk == 64 && d_v == 64) return causal ? launch<64, 64, true>(p, stream) : launch<64, 64, false>(p, stream);
+    if (d_qk == 128 && d_v == 128)
+        return causal ? launch<128, 128, true>(p, stream) : launch<128, 128, false>(p, stream);
+    if (d_qk == 192 && d_v == 128)
+        return causal ? launch<192, 128, true>(p, stream) : launch<192, 128, false>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mha

@@ -1,0 +1,83 @@
+// Kernel parameter blocks and host-side launchers of libmha (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+// One BSHD view: element strides (channel stride is 1) and the byte extent of
+// one (batch, head) slice, which bounds every buffer load from that slice.
+struct View {
+    int64_t sb, ss, sh;
+    uint32_t slice_bytes;
+};
+
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;      // may be null
+    View qv, kv, vv, ov;
+    int b, hq, hk, sq, sk;
+    int group;       // hq / hk
+    int n_mblocks;   // ceil(sq / BLOCK_M)
+    float scale_log2;  // softmax_scale * log2(e)
+};
+
+// bf16 attention forward: d_qk/d_v in {(64,64), (128,128), (192,128)}.
+hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream);
+int attn_fwd_bf16_block_m();
+
+struct GateParams {
+    const void* k;
+    View kv;
+    int b, hk, sk, d;
+    int key_stride;
+    int n_samples;   // T
+    int n_chunks;    // ceil(T / chunk)
+    float tau;
+    float* partial;  // [b*hk, n_chunks, 2, d] fp32 workspace
+    float* mean;     // [b, hk, d]
+    int32_t* gate;   // [b, hk] or null
+    bool aligned;    // 16-byte aligned rows: vector loads
+};
+
+constexpr int kGateChunk = 256;  // samples per moment chunk
+
+hipError_t launch_k_smooth_mean(const GateParams& p, hipStream_t stream);
+
+struct QuantParams {
+    const void* src;
+    View sv;
+    const float* mean;  // [b, heads, d] subtracted before quantising, or null
+    int b, heads, s, d;
+    int nblk;            // ceil(s / 128)
+    uint8_t* codes;      // [b, heads, nblk*128, d]
+    float* scales;       // [b, heads, nblk]
+};
+
+hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const QuantParams& v,
+                            hipStream_t stream);
+
+struct Fp8AttnParams {
+    const uint8_t* q;   // [b, hq, nq*128, d] codes
+    const uint8_t* k;   // [b, hk, nk*128, d]
+    const uint8_t* v;   // [b, hk, nk*128, d]
+    const float* q_scale;  // [b, hq, nq]
+    const float* k_scale;  // [b, hk, nk]
+    const float* v_scale;  // [b, hk, nk]
+    void* o;
+    View ov;
+    float* lse;
+    int b, hq, hk, sq, sk;
+    int group;
+    int nq, nk;          // token blocks of 128
+    int n_mblocks;
+    float scale_log2;
+};
+
+hipError_t launch_attn_fwd_fp8(const Fp8AttnParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace mha

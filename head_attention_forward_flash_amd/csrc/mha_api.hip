@@ -1,0 +1,261 @@
+// Host side of libmha: argument validation, workspace carving and the C ABI
+// declared in include/mha.h.  Every check runs before any launch; a refusal
+// launches nothing and records a message naming the argument.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mha.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mha_status fail(mha_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+mha_status ok() {
+    g_last_error.clear();
+    return MHA_OK;
+}
+
+mha_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;
+
+// Validates one BSHD view of `rows` rows and `d` channels of `elem` bytes and fills `out`.
+// `vec_align`: require 16-byte aligned base and rows (vector-load kernels).
+mha_status make_view(const char* name, const void* ptr, const mha_strides& st, int heads, int rows, int d,
+                     int elem, bool vec_align, mha::View* out) {
+    if (st.b < 0 || st.s < 0 || st.h < 0)
+        return fail(MHA_ERR_LAYOUT, "%s: strides must be non-negative (b=%lld s=%lld h=%lld)", name,
+                    (long long)st.b, (long long)st.s, (long long)st.h);
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(ptr);
+    if (addr % elem != 0) return fail(MHA_ERR_LAYOUT, "%s: pointer is not %d-byte aligned", name, elem);
+    if (vec_align) {
+        if (addr % 16 != 0) return fail(MHA_ERR_LAYOUT, "%s: pointer must be 16-byte aligned", name);
+        const int64_t per16 = 16 / elem;
+        if (st.b % per16 || st.s % per16 || st.h % per16)
+            return fail(MHA_ERR_LAYOUT, "%s: strides must be multiples of %lld elements (b=%lld s=%lld h=%lld)",
+                        name, (long long)per16, (long long)st.b, (long long)st.s, (long long)st.h);
+    }
+    int64_t slice = 0;
+    if (rows > 0) {
+        if (st.s > 0 && (rows - 1) > (kMaxSliceBytes / elem) / st.s)
+            return fail(MHA_ERR_OVERFLOW, "%s: one (batch, head) slice spans >= 2^31 bytes (stride.s=%lld, rows=%d)",
+                        name, (long long)st.s, rows);
+        slice = ((int64_t)(rows - 1) * st.s + d) * elem;
+        if (slice >= kMaxSliceBytes)
+            return fail(MHA_ERR_OVERFLOW, "%s: one (batch, head) slice spans >= 2^31 bytes", name);
+    }
+    (void)heads;
+    out->sb = st.b;
+    out->ss = st.s;
+    out->sh = st.h;
+    out->slice_bytes = static_cast<uint32_t>(slice);
+    return MHA_OK;
+}
+
+bool supported_bf16(int dqk, int dv) {
+    return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+}
+
+mha_status check_common(int b, int hq, int hk, int sq, int sk, float scale, int causal) {
+    if (b < 0 || sq < 0 || sk < 0) return fail(MHA_ERR_SHAPE, "b, sq, sk must be >= 0 (b=%d sq=%d sk=%d)", b, sq, sk);
+    if (hq < 1 || hk < 1) return fail(MHA_ERR_SHAPE, "hq, hk must be >= 1 (hq=%d hk=%d)", hq, hk);
+    if (hq % hk != 0) return fail(MHA_ERR_SHAPE, "hq (%d) must be a multiple of hk (%d)", hq, hk);
+    if (!std::isfinite(scale)) return fail(MHA_ERR_VALUE, "softmax_scale must be finite");
+    if (causal != 0 && causal != 1) return fail(MHA_ERR_VALUE, "causal must be 0 or 1 (got %d)", causal);
+    return MHA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_status_string(mha_status s) {
+    switch (s) {
+        case MHA_OK: return "MHA_OK";
+        case MHA_ERR_NULL: return "MHA_ERR_NULL";
+        case MHA_ERR_SHAPE: return "MHA_ERR_SHAPE";
+        case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED";
+        case MHA_ERR_LAYOUT: return "MHA_ERR_LAYOUT";
+        case MHA_ERR_OVERFLOW: return "MHA_ERR_OVERFLOW";
+        case MHA_ERR_WORKSPACE: return "MHA_ERR_WORKSPACE";
+        case MHA_ERR_HIP: return "MHA_ERR_HIP";
+        case MHA_ERR_VALUE: return "MHA_ERR_VALUE";
+    }
+    return "MHA_ERR_UNKNOWN";
+}
+
+const char* mha_last_error(void) { return g_last_error.c_str(); }
+
+mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                        const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                        int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
+                        int causal, void* stream) {
+    mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
+    if (st != MHA_OK) return st;
+    if (!supported_bf16(d_qk, d_v))
+        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (64,64) (128,128) (192,128)",
+                    d_qk, d_v);
+    if (!q) return fail(MHA_ERR_NULL, "q is NULL");
+    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (!v) return fail(MHA_ERR_NULL, "v is NULL");
+    if (!o) return fail(MHA_ERR_NULL, "o is NULL");
+    if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MHA_ERR_LAYOUT, "lse must be 4-byte aligned");
+
+    mha::AttnParams p{};
+    if ((st = make_view("q", q, q_stride, hq, sq, d_qk, 2, true, &p.qv)) != MHA_OK) return st;
+    if ((st = make_view("k", k, k_stride, hk, sk, d_qk, 2, true, &p.kv)) != MHA_OK) return st;
+    if ((st = make_view("v", v, v_stride, hk, sk, d_v, 2, true, &p.vv)) != MHA_OK) return st;
+    if ((st = make_view("o", o, o_stride, hq, sq, d_v, 2, true, &p.ov)) != MHA_OK) return st;
+
+    const int bm = mha::attn_fwd_bf16_block_m();
+    const int n_mblocks = (sq + bm - 1) / bm;
+    const int64_t nwg = int64_t(b) * hq * n_mblocks;
+    if (nwg > INT32_MAX) return fail(MHA_ERR_OVERFLOW, "grid of %lld workgroups exceeds 2^31-1", (long long)nwg);
+    if (nwg == 0) return ok();
+
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.b = b;
+    p.hq = hq;
+    p.hk = hk;
+    p.sq = sq;
+    p.sk = sk;
+    p.group = hq / hk;
+    p.n_mblocks = n_mblocks;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
+                      "attn_fwd_bf16 launch");
+}
+
+size_t k_smooth_mean_workspace_bytes(int b, int hk, int sk, int d, int key_stride, int max_keys) {
+    if (b < 0 || hk < 1 || sk < 0 || d < 1 || key_stride < 1 || max_keys < 0) return 0;
+    int64_t t = sk > 0 ? (int64_t(sk) + key_stride - 1) / key_stride : 0;
+    if (max_keys > 0 && t > max_keys) t = max_keys;
+    const int64_t chunks = (t + mha::kGateChunk - 1) / mha::kGateChunk;
+    return align256(size_t(b) * hk * (chunks > 0 ? chunks : 1) * 2 * d * sizeof(float));
+}
+
+mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int sk, int d, int key_stride,
+                         int max_keys, float tau, float* mean, int32_t* gate, void* ws, size_t ws_bytes,
+                         void* stream) {
+    if (b < 0 || sk < 0) return fail(MHA_ERR_SHAPE, "b, sk must be >= 0 (b=%d sk=%d)", b, sk);
+    if (hk < 1) return fail(MHA_ERR_SHAPE, "hk must be >= 1 (hk=%d)", hk);
+    if (d != 64 && d != 128 && d != 256) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built; supported: 64 128 256", d);
+    if (key_stride < 1) return fail(MHA_ERR_VALUE, "key_stride must be >= 1 (got %d)", key_stride);
+    if (max_keys < 0) return fail(MHA_ERR_VALUE, "max_keys must be >= 0 (got %d)", max_keys);
+    if (!std::isfinite(tau)) return fail(MHA_ERR_VALUE, "tau must be finite");
+    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (!mean) return fail(MHA_ERR_NULL, "mean is NULL");
+    if (reinterpret_cast<uintptr_t>(mean) % 4) return fail(MHA_ERR_LAYOUT, "mean must be 4-byte aligned");
+    if (gate && reinterpret_cast<uintptr_t>(gate) % 4) return fail(MHA_ERR_LAYOUT, "gate must be 4-byte aligned");
+    if (b == 0) return ok();
+
+    mha::GateParams p{};
+    mha_status st = make_view("k", k, k_stride, hk, sk, d, 2, false, &p.kv);
+    if (st != MHA_OK) return st;
+    const size_t need = k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys);
+    if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
+    if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
+
+    int64_t t = sk > 0 ? (int64_t(sk) + key_stride - 1) / key_stride : 0;
+    if (max_keys > 0 && t > max_keys) t = max_keys;
+    const int64_t n_chunks = (t + mha::kGateChunk - 1) / mha::kGateChunk;
+    if (n_chunks * b * hk > INT32_MAX)
+        return fail(MHA_ERR_OVERFLOW, "gate grid of %lld workgroups exceeds 2^31-1", (long long)(n_chunks * b * hk));
+    const uintptr_t kaddr = reinterpret_cast<uintptr_t>(k);
+    p.k = k;
+    p.b = b;
+    p.hk = hk;
+    p.sk = sk;
+    p.d = d;
+    p.key_stride = key_stride;
+    p.n_samples = static_cast<int>(t);
+    p.n_chunks = static_cast<int>((t + mha::kGateChunk - 1) / mha::kGateChunk);
+    p.tau = tau;
+    p.partial = static_cast<float*>(ws);
+    p.mean = mean;
+    p.gate = gate;
+    p.aligned = (kaddr % 16 == 0) && (k_stride.b % 8 == 0) && (k_stride.s % 8 == 0) && (k_stride.h % 8 == 0);
+    return hip_status(mha::launch_k_smooth_mean(p, static_cast<hipStream_t>(stream)), "k_smooth_mean launch");
+}
+
+mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets) {
+    if (!offsets) return fail(MHA_ERR_NULL, "offsets is NULL");
+    if (b < 0 || hq < 1 || hk < 1 || sq < 0 || sk < 0 || d < 1)
+        return fail(MHA_ERR_SHAPE, "invalid sizes for the fp8 workspace");
+    const size_t nq = (size_t(sq) + 127) / 128, nk = (size_t(sk) + 127) / 128;
+    size_t off = 0;
+    offsets[0] = off;
+    off = align256(off + size_t(b) * hq * nq * 128 * d);
+    offsets[1] = off;
+    off = align256(off + size_t(b) * hk * nk * 128 * d);
+    offsets[2] = off;
+    off = align256(off + size_t(b) * hk * nk * 128 * d);
+    offsets[3] = off;
+    off = align256(off + size_t(b) * hq * nq * 4);
+    offsets[4] = off;
+    off = align256(off + size_t(b) * hk * nk * 4);
+    offsets[5] = off;
+    return ok();
+}
+
+size_t mha_fwd_fp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d) {
+    size_t off[6];
+    if (mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, off) != MHA_OK) return 0;
+    const size_t nk = (size_t(sk) + 127) / 128;
+    return align256(off[5] + size_t(b) * hk * nk * 4);
+}
+
+mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
+                       mha_strides v_stride, const float* k_mean, void* o, mha_strides o_stride, float* lse, int b,
+                       int hq, int hk, int sq, int sk, int d, float softmax_scale, int causal, void* ws,
+                       size_t ws_bytes, void* stream) {
+    mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
+    if (st != MHA_OK) return st;
+    if (d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for fp8; supported: 128", d);
+    if (!q) return fail(MHA_ERR_NULL, "q is NULL");
+    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (!v) return fail(MHA_ERR_NULL, "v is NULL");
+    if (!o) return fail(MHA_ERR_NULL, "o is NULL");
+    if (k_mean && reinterpret_cast<uintptr_t>(k_mean) % 4) return fail(MHA_ERR_LAYOUT, "k_mean must be 4-byte aligned");
+    if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MHA_ERR_LAYOUT, "lse must be 4-byte aligned");
+    mha::View qv, kv, vv, ov;
+    if ((st = make_view("q", q, q_stride, hq, sq, d, 2, true, &qv)) != MHA_OK) return st;
+    if ((st = make_view("k", k, k_stride, hk, sk, d, 2, true, &kv)) != MHA_OK) return st;
+    if ((st = make_view("v", v, v_stride, hk, sk, d, 2, true, &vv)) != MHA_OK) return st;
+    if ((st = make_view("o", o, o_stride, hq, sq, d, 2, true, &ov)) != MHA_OK) return st;
+    const size_t need = mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d);
+    if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
+    if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
+    if (b == 0 || sq == 0) return ok();
+    return fail(MHA_ERR_UNSUPPORTED, "fp8 attention kernel not built in this library version");
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+/*
+ * mha.h - C ABI of the MI355X (gfx950) fused attention forward library (libmha.so).
+ *
+ * Three operations, each enqueued on the caller's HIP stream:
+ *
+ *   mha_fwd_bf16   fused attention forward, bf16 in / bf16 out, fp32 accumulate
+ *   k_smooth_mean  per-(batch, kv head) K mean behind a gate (two kernels, one call)
+ *   mha_fwd_fp8    K-smoothed FP8 (E4M3) block-quantised attention forward
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Tensors are BSHD views: element (b, s, h, c) lives at
+ *       base + b*stride.b + s*stride.s + h*stride.h + c        (element units)
+ *   i.e. the channel dimension is contiguous (stride 1) and the other three
+ *   strides are free (head-sliced or packed-QKV views are fine).  Strides are
+ *   non-negative.
+ *
+ *   All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   allocates no device memory and keeps no state between calls; where a call
+ *   needs scratch space the caller passes a workspace whose size is given by
+ *   the matching *_workspace_bytes() query.
+ *
+ *   `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Calls return after enqueueing; nothing synchronises.  Kernel faults
+ *   therefore surface at a later synchronisation.
+ *
+ *   Every argument is validated on the host before anything is launched; a
+ *   refusal returns a non-zero status, launches nothing, and leaves a message
+ *   naming the offending argument in mha_last_error() (thread-local).
+ *
+ *   Head mapping (GQA): query head h reads kv head h / (hq / hk).
+ *   Causal mask: top-left aligned, key j is visible to query i iff j <= i.
+ *   LSE: natural-log log-sum-exp of the scaled, masked scores of each row,
+ *   fp32, contiguous [b, hq, sq]; a row with no visible key (sk == 0) gets
+ *   O = 0 and LSE = -inf.
+ *
+ *   Results are deterministic: the same inputs give bitwise-identical outputs
+ *   (no atomics, fixed reduction orders).
+ */
+#ifndef MHA_H_
+#define MHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MHA_OK = 0,
+    MHA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+    MHA_ERR_SHAPE = 2,        /* a size is negative, or hq is not a multiple of hk   */
+    MHA_ERR_UNSUPPORTED = 3,  /* head dims / dtype combination not built             */
+    MHA_ERR_LAYOUT = 4,       /* misaligned pointer or stride, negative stride       */
+    MHA_ERR_OVERFLOW = 5,     /* an in-kernel 32-bit offset or extent would overflow  */
+    MHA_ERR_WORKSPACE = 6,    /* workspace missing, misaligned or too small          */
+    MHA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch         */
+    MHA_ERR_VALUE = 8         /* a scalar argument is out of range (non-finite scale) */
+} mha_status;
+
+/* Element strides of a BSHD view; the channel stride is 1 by contract. */
+typedef struct {
+    int64_t b;
+    int64_t s;
+    int64_t h;
+} mha_strides;
+
+/*
+ * mha_fwd_bf16 - fused attention forward pass in bf16.
+ *
+ * Computes O = softmax(softmax_scale * Q K^T + causal mask) V and the per-row
+ * LSE: the MHA forward pass of "Tune MHA config & small-head pipeline
+ * pathology" (Motivation; Test Plan: causal/non-causal, GQA 48:8, head_dim 64,
+ * and the dqk=192 / dv=128 MLA-prefill "PE" bucket).
+ *
+ *   q    [b, sq, hq, d_qk] bf16      k [b, sk, hk, d_qk] bf16
+ *   v    [b, sk, hk, d_v]  bf16      o [b, sq, hq, d_v]  bf16 (written)
+ *   lse  [b, hq, sq] fp32 contiguous (written), or NULL to skip it
+ *   (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}
+ *   b, sq, sk >= 0; hq, hk >= 1; hq % hk == 0.  b == 0 or sq == 0 is a no-op.
+ *   softmax_scale: any finite value (usually 1/sqrt(d_qk)).
+ *   causal: 0 or 1.
+ *
+ * Layout requirements: q, k, v, o 16-byte aligned and every stride a
+ * multiple of 8 elements (16-byte rows); lse 4-byte aligned.  Each (b, head)
+ * slice of q/k/v/o must span < 2^31 bytes.  Accumulation is fp32; O is
+ * rounded to bf16 once at the end.
+ */
+mha_status mha_fwd_bf16(const void* q, mha_strides q_stride,
+                        const void* k, mha_strides k_stride,
+                        const void* v, mha_strides v_stride,
+                        void* o, mha_strides o_stride,
+                        float* lse,
+                        int b, int hq, int hk, int sq, int sk, int d_qk, int d_v,
+                        float softmax_scale, int causal, void* stream);
+
+/*
+ * k_smooth_mean - the K-smoothing gate of "[HIP] Mha v4: run the K-smoothing
+ * gate as one HIP call" (Summary; commit message): per-(batch*kv head, chunk)
+ * moments over a strided key sample, then a per-head fold and a threshold,
+ * as two deterministic kernels behind one call.
+ *
+ *   k           [b, sk, hk, d] bf16 view (any 2-byte alignment; misaligned
+ *               views take a scalar-load path)
+ *   key_stride  >= 1: keys 0, key_stride, 2*key_stride, ... are sampled
+ *   max_keys    >= 0: at most this many samples (0 = no cap)
+ *   tau         gate threshold (finite)
+ *   mean        [b, hk, d] fp32 contiguous (written): the per-channel sample
+ *               mean mu where the gate is open, exactly 0 where it is closed
+ *   gate        [b, hk] int32 contiguous (written) 1 = open, 0 = closed, or NULL
+ *   ws          device workspace of at least k_smooth_mean_workspace_bytes(),
+ *               256-byte aligned; its contents on entry do not matter
+ *   d in {64, 128, 256}; b, sk >= 0; hk >= 1.
+ *
+ * Statistic: over T samples (T = ceil(sk / key_stride), capped at max_keys),
+ * mu_c = sum x / T, var_c = max(sum x^2 / T - mu_c^2, 0) in fp32 (sums kept in
+ * fp32, in a fixed order); r = sqrt(sum_c mu_c^2 / sum_c var_c) (r = +inf when
+ * the variance sum is 0 and the mean sum is not, 0 when both are 0); the gate
+ * is open iff r > tau.  T == 0 gives a closed gate and zero mean.
+ */
+size_t k_smooth_mean_workspace_bytes(int b, int hk, int sk, int d, int key_stride, int max_keys);
+
+mha_status k_smooth_mean(const void* k, mha_strides k_stride,
+                         int b, int hk, int sk, int d, int key_stride, int max_keys, float tau,
+                         float* mean, int32_t* gate,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mha_fwd_fp8 - attention forward on E4M3-quantised, K-smoothed inputs: the
+ * quantised mha_v4 call with the FP8 hd128 recipe of "[HIP] Mha v4: run the
+ * K-smoothing gate as one HIP call" (Performance table) and "MHA v4: fixes,
+ * refactor, new kernel, perf tweaks" (BF16/FP8 recipe).
+ *
+ *   q [b, sq, hq, d], k [b, sk, hk, d], v [b, sk, hk, d]: bf16 views with the
+ *     same layout requirements as mha_fwd_bf16
+ *   k_mean  [b, hk, d] fp32 contiguous (usually k_smooth_mean's output), or
+ *           NULL for no smoothing
+ *   o [b, sq, hq, d] bf16 (written); lse [b, hq, sq] fp32 or NULL
+ *   d == 128; softmax_scale finite; causal 0 or 1
+ *   ws  device workspace of at least mha_fwd_fp8_workspace_bytes(), 256-byte
+ *       aligned
+ *
+ * Steps: x_Q = fp32(Q), x_K = fp32(fp32(K) - k_mean), x_V = fp32(V); per
+ * (batch, head, block of 128 tokens): amax = max |x|, scale = amax / 448 in
+ * fp32 (1 when amax == 0), code = E4M3(x / scale) (OCP E4M3, round to nearest
+ * even, saturating at +-448).  Scores are computed on the codes with fp8 MFMA
+ * and rescaled by both block scales in fp32; P.V runs on bf16 MFMA with P
+ * rounded to bf16 and the E4M3 V codes widened exactly; the V block scale is
+ * applied in fp32.  O is rounded to bf16 once.
+ *
+ * Workspace layout (byte offsets from ws; nblk_q = ceil(sq/128), nblk_k =
+ * ceil(sk/128); every region starts 256-byte aligned):
+ *   q codes   uint8 [b, hq, nblk_q*128, d]     (token-padded, zero-filled tail)
+ *   k codes   uint8 [b, hk, nblk_k*128, d]
+ *   v codes   uint8 [b, hk, nblk_k*128, d]
+ *   q scales  fp32  [b, hq, nblk_q]
+ *   k scales  fp32  [b, hk, nblk_k]
+ *   v scales  fp32  [b, hk, nblk_k]
+ * mha_fp8_workspace_layout() reports the six offsets so callers can read the
+ * quantised tensors back.
+ */
+size_t mha_fwd_fp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d);
+
+/* Byte offsets of the six workspace regions above, in the order listed
+ * (q codes, k codes, v codes, q scales, k scales, v scales); returns
+ * MHA_ERR_SHAPE for invalid sizes. `offsets` is a host array of 6. */
+mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets);
+
+mha_status mha_fwd_fp8(const void* q, mha_strides q_stride,
+                       const void* k, mha_strides k_stride,
+                       const void* v, mha_strides v_stride,
+                       const float* k_mean,
+                       void* o, mha_strides o_stride,
+                       float* lse,
+                       int b, int hq, int hk, int sq, int sk, int d,
+                       float softmax_scale, int causal,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* mha_status_string(mha_status status);
+
+/* Thread-local message of the last refusal or failure on this thread ("" if none). */
+const char* mha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H_ */

@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every declared symbol, and refuses bad arguments.
+
+CPU only: validation happens on the host before any HIP call, so no GPU is
+touched.  Pointers passed here are fake non-null addresses that no call ever
+dereferences (every case is refused before a launch).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_attention_forward_flash_amd as mha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+S = mha.Strides
+FAKE = 0x10000      # 64 KiB-aligned fake device address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mha.load_library()
+
+
+def _header_symbols():
+    src = open(os.path.join(ROOT, "include", "mha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_header_symbol(lib):
+    syms = _header_symbols()
+    assert set(syms) == set(mha.EXPORTED_SYMBOLS), syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(lib):
+    for code, name in mha.STATUS_NAMES.items():
+        assert lib.mha_status_string(code).decode() == name
+
+
+def _bshd(s, h, d):
+    return S(s * h * d, h * d, d)
+
+
+def _bf16(lib, **kw):
+    a = dict(q=FAKE, qs=_bshd(128, 2, 64), k=FAKE, ks=_bshd(128, 2, 64), v=FAKE, vs=_bshd(128, 2, 64),
+             o=FAKE, os=_bshd(128, 2, 64), lse=None, b=1, hq=2, hk=2, sq=128, sk=128, dqk=64, dv=64,
+             scale=0.125, causal=0)
+    a.update(kw)
+    st = lib.mha_fwd_bf16(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"], a["lse"],
+                          a["b"], a["hq"], a["hk"], a["sq"], a["sk"], a["dqk"], a["dv"], a["scale"], a["causal"],
+                          None)
+    return st, lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(hq=3), 2, "multiple of hk"),
+    (dict(b=-1), 2, "b, sq, sk"),
+    (dict(hk=0), 2, "hq, hk"),
+    (dict(dqk=96, dv=96), 3, "not built"),
+    (dict(dqk=192, dv=192), 3, "not built"),
+    (dict(q=FAKE + 2), 4, "q: pointer must be 16-byte aligned"),
+    (dict(ks=S(128 * 2 * 64, 2 * 64 + 4, 64)), 4, "k: strides must be multiples"),
+    (dict(vs=S(-1, 128, 64)), 4, "v: strides must be non-negative"),
+    (dict(lse=FAKE + 2), 4, "lse must be 4-byte aligned"),
+    (dict(qs=S(0, 1 << 24, 64), sq=128), 5, "q: one (batch, head) slice"),
+    (dict(scale=float("inf")), 8, "softmax_scale"),
+    (dict(causal=2), 8, "causal"),
+])
+def test_bf16_refusals(lib, kw, status, needle):
+    st, msg = _bf16(lib, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_bf16_empty_problem_is_a_noop(lib):
+    # sq == 0 and b == 0 are accepted and launch nothing (no GPU needed)
+    assert _bf16(lib, sq=0)[0] == 0
+    assert _bf16(lib, b=0)[0] == 0
+
+
+def test_gate_refusals_and_workspace(lib):
+    need = lib.k_smooth_mean_workspace_bytes(2, 3, 1000, 128, 1, 0)
+    assert need >= 2 * 3 * 4 * 2 * 128 * 4 and need % 256 == 0
+    assert lib.k_smooth_mean_workspace_bytes(2, 3, 1000, 128, 0, 0) == 0
+
+    def call(**kw):
+        a = dict(k=FAKE, ks=_bshd(1000, 3, 128), b=2, hk=3, sk=1000, d=128, stride=1, maxk=0, tau=0.25,
+                 mean=FAKE, gate=None, ws=FAKE, wsb=need)
+        a.update(kw)
+        st = lib.k_smooth_mean(a["k"], a["ks"], a["b"], a["hk"], a["sk"], a["d"], a["stride"], a["maxk"],
+                               a["tau"], a["mean"], a["gate"], a["ws"], a["wsb"], None)
+        return st, lib.mha_last_error().decode()
+
+    assert call(k=None) == (1, "k is NULL")
+    assert call(mean=None)[0] == 1
+    assert call(d=96)[0] == 3
+    assert call(stride=0)[0] == 8
+    assert call(maxk=-1)[0] == 8
+    assert call(tau=float("nan"))[0] == 8
+    assert call(ws=None)[0] == 6
+    assert call(ws=FAKE + 128)[0] == 6
+    assert call(wsb=need - 1)[0] == 6
+    assert call(k=FAKE + 1)[0] == 4
+    assert call(b=0)[0] == 0
+
+
+def test_fp8_refusals_and_layout(lib):
+    off = mha.mha_fp8_workspace_layout(1, 16, 16, 4096, 4096, 128)
+    assert off[0] == 0 and all(o % 256 == 0 for o in off)
+    assert off[1] - off[0] >= 16 * 4096 * 128 and off[3] - off[2] >= 16 * 4096 * 128
+    need = lib.mha_fwd_fp8_workspace_bytes(1, 16, 16, 4096, 4096, 128)
+    assert need >= off[5] + 16 * 32 * 4
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, mean=None, o=FAKE, lse=None, b=1, hq=2, hk=2, sq=256, sk=256, d=128,
+                 scale=0.088, causal=0, ws=FAKE, wsb=lib.mha_fwd_fp8_workspace_bytes(1, 2, 2, 256, 256, 128))
+        a.update(kw)
+        st_ = _bshd(256, 2, 128)
+        st = lib.mha_fwd_fp8(a["q"], st_, a["k"], st_, a["v"], st_, a["mean"], a["o"], st_, a["lse"], a["b"],
+                             a["hq"], a["hk"], a["sq"], a["sk"], a["d"], a["scale"], a["causal"], a["ws"],
+                             a["wsb"], None)
+        return st, lib.mha_last_error().decode()
+
+    assert call(d=64)[0] == 3
+    assert call(v=None)[0] == 1
+    assert call(ws=None)[0] == 6
+    assert call(wsb=1024)[0] == 6
+    assert call(mean=FAKE + 2)[0] == 4
+    assert call(hq=3)[0] == 2

@@ -1,0 +1,169 @@
+"""GPU parity of mha_fwd_bf16 against the float64 oracle (needs an MI355X)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import (assert_bf16_parity, oracle_heads, require_gpu, scale_for, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, causal, scale=None):
+    import head_attention_forward_flash_amd as mha
+    dev = require_gpu()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = mha.mha_fwd_bf16(qd, kd, vd, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check_all(q, k, v, causal, what, scale=None):
+    b, sq, hq, dqk = q.shape
+    scale = scale_for(dqk) if scale is None else scale
+    o, lse = _run(q, k, v, causal, scale)
+    for bb in range(b):
+        o_ref, l_ref = oracle_heads(q, k, v, list(range(hq)), None, scale=scale, causal=causal, batch=bb)
+        assert_bf16_parity(to_np(o[bb]), o_ref, lse[bb].numpy().astype(np.float64), l_ref, f"{what} b={bb}")
+
+
+def test_tiny_d64_full():
+    w = workloads.WORKLOADS["tiny_d64"]
+    q, k, v = workloads.make_qkv(w)
+    _check_all(q, k, v, w.causal, "tiny_d64")
+
+
+SMALL_SHAPES = [
+    # b, hq, hk, sq, sk, dqk, dv
+    (2, 4, 2, 300, 300, 64, 64),
+    (1, 6, 1, 257, 257, 64, 64),
+    (1, 4, 4, 200, 333, 128, 128),
+    (2, 2, 1, 333, 200, 128, 128),
+    (1, 2, 2, 190, 190, 192, 128),
+    (1, 3, 3, 129, 65, 192, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=[f"b{s[0]}h{s[1]}/{s[2]}q{s[3]}k{s[4]}d{s[5]}-{s[6]}" for s in SMALL_SHAPES])
+def test_multi_tile_ragged(shape, causal):
+    b, hq, hk, sq, sk, dqk, dv = shape
+    seed = 1000 + sum(shape) + int(causal)
+    q = workloads.make_random((b, sq, hq, dqk), seed)
+    k = workloads.make_random((b, sk, hk, dqk), seed + 1)
+    v = workloads.make_random((b, sk, hk, dv), seed + 2)
+    _check_all(q, k, v, causal, f"shape={shape} causal={causal}")
+
+
+def _full_size_sampled(name, heads, nrows, seed):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.make_qkv(w)
+    o, lse = _run(q, k, v, w.causal, w.scale)
+    rows = workloads.sample_indices(w.sq, nrows, seed, include=[0, 1, 63, 64, 127, 128, w.sq // 2, w.sq - 1])
+    batches = sorted({0, w.b - 1})
+    for bb in batches:
+        o_ref, l_ref = oracle_heads(q, k, v, heads, rows, scale=w.scale, causal=w.causal, batch=bb)
+        o_g = to_np(o[bb][rows][:, heads])
+        l_g = lse[bb][heads][:, rows].numpy().astype(np.float64)
+        assert_bf16_parity(o_g, o_ref, l_g, l_ref, f"{name} b={bb} heads={heads}")
+
+
+def test_full_gqa_d64_causal_sampled():
+    # two query heads that share kv head 0, one from each other group edge
+    _full_size_sampled("gqa_d64_causal", [0, 1, 5, 6, 23, 47], 192, 7)
+
+
+def test_full_gqa_d128_causal_sampled():
+    _full_size_sampled("gqa_d128_causal", [0, 3, 4, 31], 192, 8)
+
+
+def test_full_mla_d192_d128_causal_sampled():
+    _full_size_sampled("mla_d192_d128_causal", [0, 77, 127], 160, 9)
+
+
+def test_value_ones_gives_ones():
+    # V = 1 everywhere: every output row is exactly 1 whatever the scores.
+    dev = require_gpu()
+    import head_attention_forward_flash_amd as mha
+    q = workloads.make_random((1, 300, 4, 128), 11, std=3.0).to(dev)
+    k = workloads.make_random((1, 300, 2, 128), 12, std=3.0).to(dev)
+    v = torch.ones((1, 300, 2, 128), dtype=torch.bfloat16, device=dev)
+    for causal in (False, True):
+        o, _ = mha.mha_fwd_bf16(q, k, v, causal=causal)
+        assert torch.all(o.float() == 1.0)
+
+
+def test_causal_row_zero_equals_v0():
+    dev = require_gpu()
+    import head_attention_forward_flash_amd as mha
+    q = workloads.make_random((2, 130, 6, 64), 21).to(dev)
+    k = workloads.make_random((2, 130, 2, 64), 22).to(dev)
+    v = workloads.make_random((2, 130, 2, 64), 23).to(dev)
+    o, lse = mha.mha_fwd_bf16(q, k, v, causal=True)
+    for h in range(6):
+        assert torch.equal(o[:, 0, h, :], v[:, 0, h // 3, :])
+    s00 = (q[:, 0].float() * k[:, 0].float().repeat_interleave(3, dim=1)).sum(-1) * 0.125
+    assert torch.allclose(lse[:, :, 0], s00, atol=1e-4, rtol=0)
+
+
+def test_strided_views_match_contiguous():
+    # Q/K/V as slices of one packed [b, s, 3, h, d] tensor, O written into a wider buffer.
+    dev = require_gpu()
+    import head_attention_forward_flash_amd as mha
+    qkv = workloads.make_random((2, 200, 3, 4, 128), 31).to(dev)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    big = torch.zeros((2, 200, 6, 128), dtype=torch.bfloat16, device=dev)
+    out = big[:, :, 1:5]
+    for causal in (False, True):
+        o1, l1 = mha.mha_fwd_bf16(q, k, v, causal=causal, out=out)
+        o2, l2 = mha.mha_fwd_bf16(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.all(big[:, :, 0] == 0) and torch.all(big[:, :, 5] == 0)
+
+
+def test_deterministic():
+    dev = require_gpu()
+    import head_attention_forward_flash_amd as mha
+    q = workloads.make_random((1, 1000, 8, 128), 41).to(dev)
+    k = workloads.make_random((1, 1000, 2, 128), 42).to(dev)
+    v = workloads.make_random((1, 1000, 2, 128), 43).to(dev)
+    a = mha.mha_fwd_bf16(q, k, v, causal=True)
+    b = mha.mha_fwd_bf16(q, k, v, causal=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_degenerate_sizes():
+    dev = require_gpu()
+    import head_attention_forward_flash_amd as mha
+    # no keys: O = 0, LSE = -inf
+    q = workloads.make_random((1, 5, 2, 64), 51).to(dev)
+    k = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = mha.mha_fwd_bf16(q, k, v, causal=False)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    # no queries / no batch: no-ops
+    q0 = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device=dev)
+    k1 = workloads.make_random((1, 7, 2, 64), 52).to(dev)
+    o, lse = mha.mha_fwd_bf16(q0, k1, k1, causal=True)
+    assert o.shape == (1, 0, 2, 64)
+    qb = torch.empty((0, 4, 2, 64), dtype=torch.bfloat16, device=dev)
+    kb = torch.empty((0, 4, 2, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = mha.mha_fwd_bf16(qb, kb, kb)
+    assert o.shape == (0, 4, 2, 64)
+    # one query, one key
+    q = workloads.make_random((1, 1, 1, 192), 53)
+    k = workloads.make_random((1, 1, 1, 192), 54)
+    v = workloads.make_random((1, 1, 1, 128), 55)
+    o, lse = _run(q, k, v, True)
+    assert torch.equal(o[0, 0, 0], v[0, 0, 0])
+    _check_all(q, k, v, False, "1x1")
+
+
+def test_large_score_magnitudes():
+    # scores of magnitude ~100: exercises the running-max updates
+    q = workloads.make_random((1, 256, 2, 64), 61, std=4.0)
+    k = workloads.make_random((1, 256, 2, 64), 62, std=4.0)
+    v = workloads.make_random((1, 256, 2, 64), 63)
+    _check_all(q, k, v, False, "large scores", scale=0.5)
+    _check_all(q, k, v, True, "large scores causal", scale=0.5)

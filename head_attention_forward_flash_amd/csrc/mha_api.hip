@@ -117,10 +117,13 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
     if (!supported_bf16(d_qk, d_v))
         return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (64,64) (128,128) (192,128)",
                     d_qk, d_v);
-    if (!q) return fail(MHA_ERR_NULL, "q is NULL");
-    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
-    if (!v) return fail(MHA_ERR_NULL, "v is NULL");
-    if (!o) return fail(MHA_ERR_NULL, "o is NULL");
+    // Empty problems need no memory: q/o may be NULL when there are no query rows, k/v when
+    // there are no keys.
+    const bool has_rows = b > 0 && sq > 0;
+    if (has_rows && !q) return fail(MHA_ERR_NULL, "q is NULL");
+    if (has_rows && sk > 0 && !k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (has_rows && sk > 0 && !v) return fail(MHA_ERR_NULL, "v is NULL");
+    if (has_rows && !o) return fail(MHA_ERR_NULL, "o is NULL");
     if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MHA_ERR_LAYOUT, "lse must be 4-byte aligned");
 
     mha::AttnParams p{};
@@ -169,8 +172,8 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int
     if (key_stride < 1) return fail(MHA_ERR_VALUE, "key_stride must be >= 1 (got %d)", key_stride);
     if (max_keys < 0) return fail(MHA_ERR_VALUE, "max_keys must be >= 0 (got %d)", max_keys);
     if (!std::isfinite(tau)) return fail(MHA_ERR_VALUE, "tau must be finite");
-    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
-    if (!mean) return fail(MHA_ERR_NULL, "mean is NULL");
+    if (!k && b > 0 && sk > 0) return fail(MHA_ERR_NULL, "k is NULL");
+    if (!mean && b > 0) return fail(MHA_ERR_NULL, "mean is NULL");
     if (reinterpret_cast<uintptr_t>(mean) % 4) return fail(MHA_ERR_LAYOUT, "mean must be 4-byte aligned");
     if (gate && reinterpret_cast<uintptr_t>(gate) % 4) return fail(MHA_ERR_LAYOUT, "gate must be 4-byte aligned");
     if (b == 0) return ok();
@@ -239,10 +242,11 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
     if (st != MHA_OK) return st;
     if (d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for fp8; supported: 128", d);
-    if (!q) return fail(MHA_ERR_NULL, "q is NULL");
-    if (!k) return fail(MHA_ERR_NULL, "k is NULL");
-    if (!v) return fail(MHA_ERR_NULL, "v is NULL");
-    if (!o) return fail(MHA_ERR_NULL, "o is NULL");
+    const bool has_rows = b > 0 && sq > 0;
+    if (has_rows && !q) return fail(MHA_ERR_NULL, "q is NULL");
+    if (has_rows && sk > 0 && !k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (has_rows && sk > 0 && !v) return fail(MHA_ERR_NULL, "v is NULL");
+    if (has_rows && !o) return fail(MHA_ERR_NULL, "o is NULL");
     if (k_mean && reinterpret_cast<uintptr_t>(k_mean) % 4) return fail(MHA_ERR_LAYOUT, "k_mean must be 4-byte aligned");
     if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MHA_ERR_LAYOUT, "lse must be 4-byte aligned");
     mha::View qv, kv, vv, ov;

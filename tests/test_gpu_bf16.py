@@ -83,7 +83,8 @@ def test_full_mla_d192_d128_causal_sampled():
 
 
 def test_value_ones_gives_ones():
-    # V = 1 everywhere: every output row is exactly 1 whatever the scores.
+    # V = 1 everywhere: every output row is 1 whatever the scores, up to the bf16 rounding of
+    # the probabilities fed to the P.V product and of O itself.
     dev = require_gpu()
     import head_attention_forward_flash_amd as mha
     q = workloads.make_random((1, 300, 4, 128), 11, std=3.0).to(dev)
@@ -91,7 +92,7 @@ def test_value_ones_gives_ones():
     v = torch.ones((1, 300, 2, 128), dtype=torch.bfloat16, device=dev)
     for causal in (False, True):
         o, _ = mha.mha_fwd_bf16(q, k, v, causal=causal)
-        assert torch.all(o.float() == 1.0)
+        assert torch.all((o.float() - 1.0).abs() <= 2.0 ** -7)
 
 
 def test_causal_row_zero_equals_v0():

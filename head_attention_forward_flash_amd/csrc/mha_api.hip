@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -259,7 +260,60 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
     if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
     if (b == 0 || sq == 0) return ok();
-    return fail(MHA_ERR_UNSUPPORTED, "fp8 attention kernel not built in this library version");
+    const int64_t nq = (int64_t(sq) + 127) / 128, nk = (int64_t(sk) + 127) / 128;
+    if (std::max(nq, nk) * 128 * d >= kMaxSliceBytes)
+        return fail(MHA_ERR_OVERFLOW, "fp8: one (batch, head) slice of codes spans >= 2^31 bytes");
+    const int64_t nwg = int64_t(b) * hq * nq;
+    const int64_t nquant = int64_t(b) * (hq * nq + 2 * hk * nk);
+    if (nwg > INT32_MAX || nquant > INT32_MAX)
+        return fail(MHA_ERR_OVERFLOW, "fp8: grid exceeds 2^31-1 workgroups");
+
+    size_t off[6];
+    mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, off);
+    char* wsb = static_cast<char*>(ws);
+    auto quant = [&](const void* src, const mha::View& sv, const float* mean, int heads, int s, int64_t nblk,
+                     size_t code_off, size_t scale_off) {
+        mha::QuantParams qp{};
+        qp.src = src;
+        qp.sv = sv;
+        qp.mean = mean;
+        qp.b = b;
+        qp.heads = heads;
+        qp.s = s;
+        qp.d = d;
+        qp.nblk = static_cast<int>(nblk);
+        qp.codes = reinterpret_cast<uint8_t*>(wsb + code_off);
+        qp.scales = reinterpret_cast<float*>(wsb + scale_off);
+        return qp;
+    };
+    const mha::QuantParams qq = quant(q, qv, nullptr, hq, sq, nq, off[0], off[3]);
+    const mha::QuantParams qk = quant(k, kv, k_mean, hk, sk, nk, off[1], off[4]);
+    const mha::QuantParams qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], off[5]);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mha::launch_quant_fp8(qq, qk, qvv, s);
+    if (e != hipSuccess) return hip_status(e, "quant_fp8 launch");
+
+    mha::Fp8AttnParams p{};
+    p.q = qq.codes;
+    p.k = qk.codes;
+    p.v = qvv.codes;
+    p.q_scale = qq.scales;
+    p.k_scale = qk.scales;
+    p.v_scale = qvv.scales;
+    p.o = o;
+    p.ov = ov;
+    p.lse = lse;
+    p.b = b;
+    p.hq = hq;
+    p.hk = hk;
+    p.sq = sq;
+    p.sk = sk;
+    p.group = hq / hk;
+    p.nq = static_cast<int>(nq);
+    p.nk = static_cast<int>(nk);
+    p.n_mblocks = static_cast<int>(nq);
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return hip_status(mha::launch_attn_fwd_fp8(p, d, causal != 0, s), "attn_fwd_fp8 launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,124 @@
+// FP8 (OCP E4M3) block quantisation of Q, K - mean and V for the quantised
+// attention call: the producer side of the FP8 hd128 mha_v4 recipe of
+// "[HIP] Mha v4: run the K-smoothing gate as one HIP call" (Summary: K is
+// smoothed by its per-head mean before quantisation; Performance table: FP8
+// hd128) and "MHA v4: fixes, refactor, new kernel, perf tweaks" (BF16/FP8
+// recipe, quantisation producers).
+//
+// One workgroup per (tensor, batch, head, block of 128 tokens):
+//   x      = fp32(bf16 input)                 (K: fp32(K) - mean[b, h, c], one fp32 rounding)
+//   amax   = max |x| over the block's tokens and channels (wave max, then LDS)
+//   scale  = amax / 448 in fp32 (1 when amax == 0)
+//   code   = E4M3(x / scale): IEEE fp32 division, clamp to +-448 (a no-op except
+//            for the last half-ulp above 448, which rounds to 448 anyway), then
+//            v_cvt_pk_fp8_f32 (round to nearest even)
+// Codes go to a token-padded [b, h, nblk*128, D] array (tokens past s are
+// written as zero codes), scales to [b, h, nblk].  HBM-bound: 2 bytes read and
+// 1 byte written per element.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mha {
+namespace {
+
+constexpr int NT = 256;
+constexpr int TOK = 128;
+
+template <int D>
+__device__ __forceinline__ void quant_block(const QuantParams& p, int bh_blk, float* red) {
+    constexpr int TPR = D / 8;          // threads per token row (16 B each)
+    constexpr int ROWS = NT / TPR;      // token rows per pass
+    constexpr int PASSES = TOK / ROWS;
+    const int blk = bh_blk % p.nblk;
+    const int bh = bh_blk / p.nblk;
+    const int h = bh % p.heads, bb = bh / p.heads;
+    const int tid = threadIdx.x;
+    const int c0 = (tid % TPR) * 8;
+    const int r0 = tid / TPR;
+
+    const char* base = static_cast<const char*>(p.src) + 2 * (bb * p.sv.sb + h * p.sv.sh);
+    const auto rs = make_rsrc(base, p.sv.slice_bytes);
+
+    float mu[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mu[i] = 0.f;
+    if (p.mean != nullptr) {
+        const float* m = p.mean + static_cast<int64_t>(bh) * D + c0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mu[i] = m[i];
+    }
+
+    float x[PASSES][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int tok = blk * TOK + ps * ROWS + r0;
+        const uint32_t off = tok < p.s ? static_cast<uint32_t>((tok * p.sv.ss + c0) * 2) : kOutOfRange;
+        const u32x4 w = buffer_load_b128(rs, off);
+        const bool live = tok < p.s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_bits_to_float(w[i] & 0xffffu);
+            const float hi = bf16_bits_to_float(w[i] >> 16);
+            x[ps][2 * i] = live ? lo - mu[2 * i] : 0.f;
+            x[ps][2 * i + 1] = live ? hi - mu[2 * i + 1] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ps][i]));
+    }
+    // block max: within the wave, then across the 4 waves through LDS
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+
+    uint8_t* codes = p.codes + (static_cast<int64_t>(bh) * p.nblk * TOK + blk * TOK) * D;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        uint32_t packed[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[ps][half * 4 + j] / scale, -448.f), 448.f);
+            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wv, true);
+            packed[half] = static_cast<uint32_t>(wv);
+        }
+        const int row = ps * ROWS + r0;
+        *reinterpret_cast<u32x2*>(codes + row * D + c0) = u32x2{packed[0], packed[1]};
+    }
+    if (tid == 0) p.scales[static_cast<int64_t>(bh) * p.nblk + blk] = scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void quant_fp8_kernel(const QuantParams q, const QuantParams k,
+                                                       const QuantParams v) {
+    __shared__ float red[4];
+    const int nq = q.b * q.heads * q.nblk;
+    const int nk = k.b * k.heads * k.nblk;
+    int id = blockIdx.x;
+    if (id < nq) {
+        quant_block<D>(q, id, red);
+    } else if ((id -= nq) < nk) {
+        quant_block<D>(k, id, red);
+    } else {
+        quant_block<D>(v, id - nk, red);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const QuantParams& v, hipStream_t stream) {
+    const int64_t total = int64_t(q.b) * q.heads * q.nblk + int64_t(k.b) * k.heads * k.nblk +
+                          int64_t(v.b) * v.heads * v.nblk;
+    if (total == 0) return hipSuccess;
+    if (q.d != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_fp8_kernel<128>), dim3(static_cast<unsigned>(total)), dim3(NT), 0, stream, q, k, v);
+    return hipGetLastError();
+}
+
+}  // namespace mha

@@ -1,0 +1,133 @@
+"""GPU parity of the quantised path: E4M3 block codes (bit-exact) and FP8 attention (needs an MI355X)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import FP8_REL_L2, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_call(q, k, v, mu, causal):
+    """Run mha_fwd_fp8 on device copies; return (o, lse, quantised tensors read back from the workspace)."""
+    import head_attention_forward_flash_amd as mha
+    dev = require_gpu()
+    b, sq, hq, d = q.shape
+    _, sk, hk, _ = k.shape
+    mu_d = None if mu is None else torch.from_numpy(np.ascontiguousarray(mu, dtype=np.float32)).to(dev)
+    o, lse, ws = mha.mha_fwd_fp8(q.to(dev), k.to(dev), v.to(dev), k_mean=mu_d, causal=causal)
+    torch.cuda.synchronize()
+    off = mha.mha_fp8_workspace_layout(b, hq, hk, sq, sk, d)
+    nq, nk = (sq + 127) // 128, (sk + 127) // 128
+    wsc = ws.cpu().numpy()
+
+    def codes(i, heads, n, s):
+        raw = wsc[off[i]: off[i] + b * heads * n * 128 * d].reshape(b, heads, n * 128, d)
+        return raw[:, :, :s, :].transpose(0, 2, 1, 3)          # -> [b, s, h, d]
+
+    def scales(i, heads, n):
+        return wsc[off[i]: off[i] + b * heads * n * 4].view(np.float32).reshape(b, heads, n)
+
+    quant = {"q": (codes(0, hq, nq, sq), scales(3, hq, nq)), "k": (codes(1, hk, nk, sk), scales(4, hk, nk)),
+             "v": (codes(2, hk, nk, sk), scales(5, hk, nk))}
+    pad = {"q": wsc[off[0]: off[0] + b * hq * nq * 128 * d].reshape(b, hq, nq * 128, d)[:, :, sq:],
+           "k": wsc[off[1]: off[1] + b * hk * nk * 128 * d].reshape(b, hk, nk * 128, d)[:, :, sk:]}
+    return o.cpu(), lse.cpu(), quant, pad
+
+
+def _rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _inputs(b, sq, sk, hq, hk, d, seed, bias_std=3.0):
+    q = workloads.make_random((b, sq, hq, d), seed)
+    k = workloads.make_random((b, sk, hk, d), seed + 1, dtype=torch.float32)
+    bias = workloads.make_random((1, 1, hk, d), seed + 2, dtype=torch.float32) * bias_std
+    k = (k + bias).to(torch.bfloat16)
+    v = workloads.make_random((b, sk, hk, d), seed + 3)
+    return q, k, v
+
+
+def _oracle_mu(k):
+    return oracle.k_smooth_mean(k.float().numpy())["mean"].astype(np.float32)
+
+
+@pytest.mark.parametrize("smooth", [True, False])
+def test_quantised_codes_and_scales_bit_exact(smooth):
+    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 500)
+    mu = _oracle_mu(k) if smooth else None
+    _, _, quant, pad = _fp8_call(q, k, v, mu, causal=False)
+    ref_in = {"q": q.float().numpy(), "k": oracle.fp8.smooth_k(k.float().numpy(), mu), "v": v.float().numpy()}
+    for name in ("q", "k", "v"):
+        codes_ref, scales_ref, _ = oracle.quantize_blocks(ref_in[name])
+        codes_gpu, scales_gpu = quant[name]
+        np.testing.assert_array_equal(scales_gpu, scales_ref, err_msg=f"{name} scales")
+        mism = int((codes_gpu != codes_ref).sum())
+        assert mism == 0, f"{name}: {mism} of {codes_ref.size} E4M3 codes differ"
+    assert (pad["q"] == 0).all() and (pad["k"] == 0).all(), "token padding must be zero codes"
+
+
+def _check_attention(q, k, v, mu, causal, what, heads=None):
+    o, lse, _, _ = _fp8_call(q, k, v, mu, causal)
+    d = q.shape[3]
+    o_ref, lse_ref, _ = oracle.fp8_attention_forward(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                                     mu=mu, scale=d ** -0.5, causal=causal, heads=heads)
+    o_g = o.float().numpy().astype(np.float64)
+    l_g = lse.numpy().astype(np.float64)
+    if heads is not None:
+        o_g, l_g = o_g[:, :, heads], l_g[:, heads]
+    rel = _rel_l2(o_g, o_ref)
+    lerr = float(np.abs(l_g - lse_ref).max())
+    exact, _ = oracle.attention_forward(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                        scale=d ** -0.5, causal=causal, heads=heads)
+    print(f"[fp8] {what}: rel_l2 vs same-quantisation oracle {rel:.3e}, vs unquantised {_rel_l2(o_g, exact):.3e}, "
+          f"lse max-abs {lerr:.3e}", flush=True)
+    assert rel <= FP8_REL_L2, f"{what}: rel-L2 {rel:.4e} > {FP8_REL_L2}"
+    return rel
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_gqa(causal):
+    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 600)
+    _check_attention(q, k, v, _oracle_mu(k), causal, f"ragged gqa causal={causal}")
+
+
+def test_no_smoothing():
+    q, k, v = _inputs(1, 256, 384, 2, 2, 128, 700, bias_std=0.0)
+    _check_attention(q, k, v, None, False, "no smoothing")
+
+
+def test_full_fp8_workload_sampled_heads():
+    w = workloads.WORKLOADS["fp8_ksmooth_d128"]
+    q, k, v = workloads.make_qkv(w)
+    mu = _oracle_mu(k)
+    _check_attention(q, k, v, mu, w.causal, "fp8 workload", heads=[0, 7, 15])
+
+
+def test_gpu_gate_then_fp8_matches_oracle_pipeline():
+    # The whole quantised call: GPU gate -> GPU fp8 attention, against oracle gate -> oracle fp8.
+    import head_attention_forward_flash_amd as mha
+    dev = require_gpu()
+    q, k, v = _inputs(1, 512, 512, 4, 4, 128, 800)
+    kd = k.to(dev)
+    mean, gate = mha.k_smooth_mean(kd)
+    o, _, _ = mha.mha_fwd_fp8(q.to(dev), kd, v.to(dev), k_mean=mean)
+    torch.cuda.synchronize()
+    mu_ref = _oracle_mu(k)
+    assert gate.cpu().numpy().all()
+    o_ref, _, _ = oracle.fp8_attention_forward(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                               mu=mu_ref, scale=128 ** -0.5, causal=False)
+    rel = _rel_l2(o.cpu().float().numpy(), o_ref)
+    print(f"[fp8] gate+fp8 pipeline rel_l2={rel:.3e}", flush=True)
+    assert rel <= FP8_REL_L2
+
+
+def test_fp8_deterministic():
+    q, k, v = _inputs(1, 400, 400, 2, 2, 128, 900)
+    mu = _oracle_mu(k)
+    a = _fp8_call(q, k, v, mu, True)
+    b = _fp8_call(q, k, v, mu, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -20,12 +20,18 @@
 //   V      64 x d_v tile written TRANSPOSED into LDS (channel-major, keys
 //          contiguous) so the A operand of O^T = V^T P^T is two ds_read_b64.
 //   tiles  global -> registers for tile t+1 is issued before computing tile t
-//          (register double buffering); LDS holds one tile.
+//          (register double buffering); LDS holds one tile.  Each tile's loads
+//          use a buffer resource based at the tile, so their offsets are
+//          loop-invariant and the hardware zero-fills keys past sk.
 //   causal key tiles past the block's last row are never loaded; masking is
 //          applied only on tiles that cross the diagonal or the ragged end.
-//   softmax online, in base 2 (scores pre-multiplied by scale*log2 e); the
-//          running max is only moved when a row's max grows by more than 8
-//          (a factor 256), which keeps O and l consistent and rescales rarely.
+//   softmax online, in base 2: p = exp2(s*c - m*c) with c = |scale| * log2 e
+//          folded into one FMA (a negative scale negates Q, which is exact);
+//          the running max is only moved when a row's max grows by more than
+//          a factor 2^8 in probability, which keeps O and l consistent and
+//          rescales rarely; the row sum adds the bf16-rounded probabilities
+//          that enter P.V (v_dot2_f32_bf16), so O is normalised by exactly
+//          the weights it was built from.
 //
 // Every global load goes through a buffer resource clamped to the (batch, head)
 // slice, so rows past sq / sk read as zero instead of faulting.
@@ -78,8 +84,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     const char* kbase = static_cast<const char*>(p.k) + 2 * (bb * p.kv.sb + g * p.kv.sh);
     const char* vbase = static_cast<const char*>(p.v) + 2 * (bb * p.vv.sb + g * p.vv.sh);
     const auto qrs = make_rsrc(qbase, p.qv.slice_bytes);
-    const auto krs = make_rsrc(kbase, p.kv.slice_bytes);
-    const auto vrs = make_rsrc(vbase, p.vv.slice_bytes);
 
     const int wave_row0 = mblk * BM + wave * 32;
     const int my_row = wave_row0 + col;
@@ -91,9 +95,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
-            qf[kk] = __builtin_bit_cast(bf16x8, buffer_load_b128(qrs, off));
+            u32x4 w = buffer_load_b128(qrs, off);
+            // softmax(c * s) with c < 0 equals softmax(|c| * (-s)): negate Q (exact) and use |c|
+            if (p.scale_log2 < 0.f) w ^= 0x80008000u;
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
+    const float c = fabsf(p.scale_log2);   // base-2 score scale, >= 0
 
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
@@ -104,32 +112,38 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     const int vkg = tid % VKGROUPS;   // key group (VKEYS consecutive keys)
     const int vcg = tid / VKGROUPS;   // 8-channel group
 
-    auto load_tile = [&](int t) {
-        const int key0 = t * BN;
+    // Per-thread byte offsets inside a tile (constant over the loop).  Each tile gets its own
+    // buffer resource starting at its first key and clamped to the slice end, so keys past sk
+    // (rows are disjoint: stride.s >= d, checked on the host) read as zero with no per-key test.
+    uint32_t koff[KCHUNKS];
 #pragma unroll
-        for (int i = 0; i < KCHUNKS; ++i) {
-            const int c = tid + NTHREADS * i;
-            const int row = c / (DQK / 8);
-            const int ch = c % (DQK / 8);
-            const int key = key0 + row;
-            const uint32_t off = key < p.sk ? static_cast<uint32_t>(key * p.kv.ss * 2 + ch * 16) : kOutOfRange;
-            kreg[i] = buffer_load_b128(krs, off);
-        }
+    for (int i = 0; i < KCHUNKS; ++i) {
+        const int chunk = tid + NTHREADS * i;
+        koff[i] = static_cast<uint32_t>((chunk / (DQK / 8)) * p.kv.ss * 2 + (chunk % (DQK / 8)) * 16);
+    }
+    uint32_t voff[VKEYS];
 #pragma unroll
-        for (int i = 0; i < VKEYS; ++i) {
-            const int key = key0 + vkg * VKEYS + i;
-            const uint32_t off = key < p.sk ? static_cast<uint32_t>(key * p.vv.ss * 2 + vcg * 16) : kOutOfRange;
-            vreg[i] = buffer_load_b128(vrs, off);
-        }
-    };
+    for (int i = 0; i < VKEYS; ++i) voff[i] = static_cast<uint32_t>((vkg * VKEYS + i) * p.vv.ss * 2 + vcg * 16);
 
+    auto tile_rsrc = [&](const char* base, const View& vw, int t) {
+        const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
+        const uint32_t left = start < static_cast<int64_t>(vw.slice_bytes)
+                                  ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
+        return make_rsrc(left ? base + start : base, left);
+    };
+    auto load_tile = [&](int t) {
+        const auto kr = tile_rsrc(kbase, p.kv, t);
+        const auto vr = tile_rsrc(vbase, p.vv, t);
+#pragma unroll
+        for (int i = 0; i < KCHUNKS; ++i) kreg[i] = buffer_load_b128(kr, koff[i]);
+#pragma unroll
+        for (int i = 0; i < VKEYS; ++i) vreg[i] = buffer_load_b128(vr, voff[i]);
+    };
     auto store_tile = [&]() {
 #pragma unroll
         for (int i = 0; i < KCHUNKS; ++i) {
-            const int c = tid + NTHREADS * i;
-            const int row = c / (DQK / 8);
-            const int ch = c % (DQK / 8);
-            *reinterpret_cast<u32x4*>(&k_lds[row * KROW + ch * 8]) = kreg[i];
+            const int chunk = tid + NTHREADS * i;
+            *reinterpret_cast<u32x4*>(&k_lds[(chunk / (DQK / 8)) * KROW + (chunk % (DQK / 8)) * 8]) = kreg[i];
         }
         // V^T: channel (vcg*8 + e) row receives keys vkg*VKEYS .. +VKEYS
 #pragma unroll
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     f32x16 oacc[CBLK];
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
-    float m_run = kNegInf;   // running max (log2 units), same in lane and lane^32
+    float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
     if (ntiles > 0) load_tile(0);
@@ -164,50 +178,67 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         __syncthreads();
         store_tile();
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+        load_tile(t + 1);   // past the last tile this loads nothing (empty buffer range)
 
-        // ---- S^T = K Q^T for two 32-key blocks
-        f32x16 s[2];
+        // ---- S^T = K Q^T: two independent 32-key accumulators.  K fragments are read
+        //      KAHEAD k-steps ahead of the MFMAs that use them; the scheduling fences keep
+        //      the compiler from sinking the reads next to their use.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        {
+            constexpr int KAHEAD = 3;
+            const uint16_t* krow0 = &k_lds[col * KROW + half * 8];
+            const uint16_t* krow1 = krow0 + 32 * KROW;
+            bf16x8 fa[KSTEPS], fb[KSTEPS];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-            const uint16_t* krow = &k_lds[(kb * 32 + col) * KROW + half * 8];
+            for (int kk = 0; kk < KAHEAD && kk < KSTEPS; ++kk) {
+                fa[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow0 + kk * 16));
+                fb[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow1 + kk * 16));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + kk * 16));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+                if (kk + KAHEAD < KSTEPS) {
+                    fa[kk + KAHEAD] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow0 + (kk + KAHEAD) * 16));
+                    fb[kk + KAHEAD] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow1 + (kk + KAHEAD) * 16));
+                }
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], qf[kk], s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], qf[kk], s[1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        // ---- scale, mask, tile max
+        // ---- mask (tiles crossing the diagonal or the ragged end only), tile max of raw scores
         const int key0 = t * BN;
         const bool need_mask = (key0 + BN > p.sk) || (CAUSAL && key0 + BN - 1 > wave_row0);
-        float mt = kNegInf;
+        if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float x = s[kb][j] * p.scale_log2;
-                if (need_mask) {
+                for (int j = 0; j < 16; ++j) {
                     const int key = key0 + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                    if (key >= p.sk || (CAUSAL && key > my_row)) x = kNegInf;
+                    if (key >= p.sk || (CAUSAL && key > my_row)) s[kb][j] = kNegInf;
                 }
-                s[kb][j] = x;
-                mt = fmaxf(mt, x);
             }
         }
+        float mt = __builtin_fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int j = 2; j < 16; j += 2) mt = max3(mt, s[0][j], s[0][j + 1]);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) mt = max3(mt, s[1][j], s[1][j + 1]);
         mt = fmaxf(mt, swap_halves(mt));
 
-        // ---- online softmax with lazy rescaling
+        // ---- online softmax with lazy rescaling (the reference max only moves when a row's
+        //      max grows by more than 2^8 in probability)
         const float m_new = fmaxf(m_run, mt);
-        if (__any(m_new > m_run + kRescaleThreshold)) {
-            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        const bool grow = m_new > m_run && (m_run == kNegInf || (m_new - m_run) * c > kRescaleThreshold);
+        if (__any(grow)) {
+            const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
             l_run *= alpha;
 #pragma unroll
             for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
             m_run = m_new;
         }
-        const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
 
         bf16x8 pf[4];
 #pragma unroll
@@ -215,24 +246,44 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p0 = fast_exp2(s[ks >> 1][(ks & 1) * 8 + 2 * i] - m_use);
-                const float p1 = fast_exp2(s[ks >> 1][(ks & 1) * 8 + 2 * i + 1] - m_use);
-                l_run += p0 + p1;
+                const float s0 = s[ks >> 1][(ks & 1) * 8 + 2 * i];
+                const float s1 = s[ks >> 1][(ks & 1) * 8 + 2 * i + 1];
+                float p0 = fast_exp2(fmaf(s0, c, -mc));
+                float p1 = fast_exp2(fmaf(s1, c, -mc));
+                if (need_mask) {   // masked keys give exactly 0 whatever c is
+                    p0 = s0 == kNegInf ? 0.f : p0;
+                    p1 = s1 == kNegInf ? 0.f : p1;
+                }
                 w[i] = pack_bf16x2(p0, p1);
+                l_run = add_bf16_pair(w[i], l_run);   // the row sum of the rounded P fed to P.V
             }
             pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T: per 16-key step, CBLK independent accumulators; the V
+        //      fragments of step ks+1 are read while the MFMAs of step ks run
+        {
+            const uint16_t* vrow = &v_lds[col * VROW + half * 4];
+            auto vfrag = [&](int cb, int ks) {
+                const uint16_t* vr = vrow + cb * 32 * VROW + ks * 16;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+                return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            };
+            bf16x8 a[2][CBLK];
 #pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-            const uint16_t* vrow = &v_lds[(cb * 32 + col) * VROW + half * 4];
+            for (int cb = 0; cb < CBLK; ++cb) a[0][cb] = vfrag(cb, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
+                if (ks + 1 < 4) {
+#pragma unroll
+                    for (int cb = 0; cb < CBLK; ++cb) a[(ks + 1) & 1][cb] = vfrag(cb, ks + 1);
+                }
+#pragma unroll
+                for (int cb = 0; cb < CBLK; ++cb)
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][cb], pf[ks], oacc[cb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -253,7 +304,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
             }
         }
         if (p.lse != nullptr && half == 0) {
-            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+            const float lse = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
             p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
         }
     }

@@ -55,7 +55,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value held by lane (lane ^ 32): the two halves of a wave64 exchange one dword.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Value held by lane (lane ^ 32).  v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second; with both operands equal, a lane of the
+// lower half finds its partner's value in the second result and a lane of the upper half in
+// the first.
+__device__ __forceinline__ float swap_halves(float x) {
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+
+// acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
 
 }  // namespace mha

@@ -132,6 +132,12 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
     if ((st = make_view("k", k, k_stride, hk, sk, d_qk, 2, true, &p.kv)) != MHA_OK) return st;
     if ((st = make_view("v", v, v_stride, hk, sk, d_v, 2, true, &p.vv)) != MHA_OK) return st;
     if ((st = make_view("o", o, o_stride, hq, sq, d_v, 2, true, &p.ov)) != MHA_OK) return st;
+    // The kernel zero-fills keys past sk by bounding each tile's loads at the slice end, which
+    // needs key rows that do not overlap.
+    if (sk > 1 && k_stride.s < d_qk)
+        return fail(MHA_ERR_LAYOUT, "k: rows overlap (stride.s = %lld < d_qk = %d)", (long long)k_stride.s, d_qk);
+    if (sk > 1 && v_stride.s < d_v)
+        return fail(MHA_ERR_LAYOUT, "v: rows overlap (stride.s = %lld < d_v = %d)", (long long)v_stride.s, d_v);
 
     const int bm = mha::attn_fwd_bf16_block_m();
     const int n_mblocks = (sq + bm - 1) / bm;

@@ -83,7 +83,8 @@ typedef struct {
  *   causal: 0 or 1.
  *
  * Layout requirements: q, k, v, o 16-byte aligned and every stride a
- * multiple of 8 elements (16-byte rows); lse 4-byte aligned.  Each (b, head)
+ * multiple of 8 elements (16-byte rows); key rows of k and v must not overlap
+ * (stride.s >= d when sk > 1); lse 4-byte aligned.  Each (b, head)
  * slice of q/k/v/o must span < 2^31 bytes.  Accumulation is fp32; O is
  * rounded to bf16 once at the end.
  */

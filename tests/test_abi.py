@@ -69,6 +69,7 @@ def _bf16(lib, **kw):
     (dict(vs=S(-1, 128, 64)), 4, "v: strides must be non-negative"),
     (dict(lse=FAKE + 2), 4, "lse must be 4-byte aligned"),
     (dict(qs=S(0, 1 << 24, 64), sq=128), 5, "q: one (batch, head) slice"),
+    (dict(ks=S(128 * 2 * 64, 32, 64)), 4, "k: rows overlap"),
     (dict(scale=float("inf")), 8, "softmax_scale"),
     (dict(causal=2), 8, "causal"),
 ])

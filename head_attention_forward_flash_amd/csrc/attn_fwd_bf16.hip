@@ -36,6 +36,8 @@
 // Every global load goes through a buffer resource clamped to the (batch, head)
 // slice, so rows past sq / sk read as zero instead of faulting.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,6 +51,8 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
+    // K/V tiles in flight: two for d_qk = 64 (short tiles cannot hide a load), else one
+    constexpr int PF = DQK == 64 ? 2 : 1;
     constexpr int KROW = DQK + 8;             // K row in LDS, elements (16-byte pad)
     constexpr int VROW = BN + 4;              // V^T row in LDS, elements (8-byte pad)
     constexpr int KSTEPS = DQK / 16;          // MFMA k-steps for S^T
@@ -106,9 +110,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // ---- staging registers for one K/V tile
-    u32x4 kreg[KCHUNKS];
-    u32x4 vreg[VKEYS];
+    // ---- staging registers: PF tiles of K/V in flight (loads of tile t+PF are issued while
+    //      tile t is computed)
+    u32x4 kreg[PF][KCHUNKS];
+    u32x4 vreg[PF][VKEYS];
     const int vkg = tid % VKGROUPS;   // key group (VKEYS consecutive keys)
     const int vcg = tid / VKGROUPS;   // 8-channel group
 
@@ -131,19 +136,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
                                   ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
-    auto load_tile = [&](int t) {
+    auto load_tile = [&](int t, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
         const auto kr = tile_rsrc(kbase, p.kv, t);
         const auto vr = tile_rsrc(vbase, p.vv, t);
 #pragma unroll
-        for (int i = 0; i < KCHUNKS; ++i) kreg[i] = buffer_load_b128(kr, koff[i]);
+        for (int i = 0; i < KCHUNKS; ++i) kreg[slot][i] = buffer_load_b128(kr, koff[i]);
 #pragma unroll
-        for (int i = 0; i < VKEYS; ++i) vreg[i] = buffer_load_b128(vr, voff[i]);
+        for (int i = 0; i < VKEYS; ++i) vreg[slot][i] = buffer_load_b128(vr, voff[i]);
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
         for (int i = 0; i < KCHUNKS; ++i) {
             const int chunk = tid + NTHREADS * i;
-            *reinterpret_cast<u32x4*>(&k_lds[(chunk / (DQK / 8)) * KROW + (chunk % (DQK / 8)) * 8]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&k_lds[(chunk / (DQK / 8)) * KROW + (chunk % (DQK / 8)) * 8]) = kreg[slot][i];
         }
         // V^T: channel (vcg*8 + e) row receives keys vkg*VKEYS .. +VKEYS
 #pragma unroll
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
             uint32_t w[VKEYS / 2];
 #pragma unroll
             for (int i = 0; i < VKEYS / 2; ++i) {
-                const uint32_t a = vreg[2 * i][dw];
-                const uint32_t c2 = vreg[2 * i + 1][dw];
+                const uint32_t a = vreg[slot][2 * i][dw];
+                const uint32_t c2 = vreg[slot][2 * i + 1][dw];
                 w[i] = hi ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
             }
             uint16_t* dst = &v_lds[(vcg * 8 + e) * VROW + vkg * VKEYS];
@@ -172,14 +179,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
-    if (ntiles > 0) load_tile(0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        load_tile(t + 1);   // past the last tile this loads nothing (empty buffer range)
-
+    auto compute_tile = [&](int t) {
         // ---- S^T = K Q^T: two independent 32-key accumulators.  K fragments are read
         //      KAHEAD k-steps ahead of the MFMAs that use them; the scheduling fences keep
         //      the compiler from sinking the reads next to their use.
@@ -286,6 +286,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+
+    // tiles past the last one load nothing (their buffer range is empty)
+    load_tile(0, std::integral_constant<int, 0>{});
+    if constexpr (PF > 1) load_tile(1, std::integral_constant<int, 1>{});
+    for (int t0 = 0; t0 < ntiles; t0 += PF) {
+        auto step = [&](auto slot_c) {
+            constexpr int slot = decltype(slot_c)::value;
+            const int t = t0 + slot;
+            if (t < ntiles) {
+                __syncthreads();
+                store_tile(slot_c);
+                __syncthreads();
+                load_tile(t + PF, slot_c);
+                compute_tile(t);
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        if constexpr (PF > 1) step(std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE

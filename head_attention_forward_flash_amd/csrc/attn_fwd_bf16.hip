@@ -130,13 +130,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 #pragma unroll
     for (int i = 0; i < VKEYS; ++i) voff[i] = static_cast<uint32_t>((vkg * VKEYS + i) * p.vv.ss * 2 + vcg * 16);
 
-    auto tile_rsrc = [&](const char* base, const View& vw, int t) {
+    auto tile_rsrc = [&](const char* base, const View& vw, int t) __attribute__((always_inline)) {
         const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
         const uint32_t left = start < static_cast<int64_t>(vw.slice_bytes)
                                   ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
-    auto load_tile = [&](int t, auto slot_c) {
+    auto load_tile = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
         const auto kr = tile_rsrc(kbase, p.kv, t);
         const auto vr = tile_rsrc(vbase, p.vv, t);
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 #pragma unroll
         for (int i = 0; i < VKEYS; ++i) vreg[slot][i] = buffer_load_b128(vr, voff[i]);
     };
-    auto store_tile = [&](auto slot_c) {
+    auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
         for (int i = 0; i < KCHUNKS; ++i) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
-    auto compute_tile = [&](int t) {
+    auto compute_tile = [&](int t) __attribute__((always_inline)) {
         // ---- S^T = K Q^T: two independent 32-key accumulators.  K fragments are read
         //      KAHEAD k-steps ahead of the MFMAs that use them; the scheduling fences keep
         //      the compiler from sinking the reads next to their use.
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         //      fragments of step ks+1 are read while the MFMAs of step ks run
         {
             const uint16_t* vrow = &v_lds[col * VROW + half * 4];
-            auto vfrag = [&](int cb, int ks) {
+            auto vfrag = [&](int cb, int ks) __attribute__((always_inline)) {
                 const uint16_t* vr = vrow + cb * 32 * VROW + ks * 16;
                 const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
                 const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     load_tile(0, std::integral_constant<int, 0>{});
     if constexpr (PF > 1) load_tile(1, std::integral_constant<int, 1>{});
     for (int t0 = 0; t0 < ntiles; t0 += PF) {
-        auto step = [&](auto slot_c) {
+        auto step = [&](auto slot_c) __attribute__((always_inline)) {
             constexpr int slot = decltype(slot_c)::value;
             const int t = t0 + slot;
             if (t < ntiles) {

@@ -43,6 +43,21 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def check_exports(path: str) -> None:
+    """Refuse a library whose host objects reference kernel stubs they never defined.
+
+    A host-side compile that silently drops a kernel's launch stub leaves an undefined
+    symbol that only shows up when the library is loaded; catch it at build time.
+    """
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "_ZN3mha" in ln]
+    if missing:
+        raise RuntimeError("libmha.so has undefined internal symbols: " + ", ".join(missing))
+
+
 def build(verbose: bool = False, save_temps: str | None = None, jobs: int = 8) -> str:
     cc = hipcc()
     srcs = sources()
@@ -74,6 +89,7 @@ def build(verbose: bool = False, save_temps: str | None = None, jobs: int = 8) -
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        check_exports(out_tmp)
         os.replace(out_tmp, LIB_PATH)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)

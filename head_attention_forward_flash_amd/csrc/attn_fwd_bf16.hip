@@ -51,20 +51,18 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
-    // K/V tiles in flight: two for d_qk = 64 (short tiles cannot hide a load), else one
-    constexpr int PF = DQK == 64 ? 2 : 1;
-    constexpr int KROW = DQK + 8;             // K row in LDS, elements (16-byte pad)
-    constexpr int VROW = BN + 4;              // V^T row in LDS, elements (8-byte pad)
+    constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
+    constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
+    constexpr int KTILE = BN * KROWB;
+    constexpr int VTILE = BN * VROWB;
+    constexpr int STAGE = KTILE + VTILE;      // one LDS stage: a K tile then a V tile
+    constexpr int KDMA = KTILE / 1024 / 4;    // 1 KiB DMA blocks per wave per K tile
+    constexpr int VDMA = VTILE / 1024 / 4;
     constexpr int KSTEPS = DQK / 16;          // MFMA k-steps for S^T
-    constexpr int KCHUNKS = DQK / 32;         // 16-byte K chunks per thread per tile
-    constexpr int VKEYS = DV / 32;            // keys per thread when staging V (4 or 2)
-    constexpr int VKGROUPS = BN / VKEYS;      // key groups per tile
     constexpr int CBLK = DV / 32;             // 32-channel output blocks
-    static_assert(BN * DQK / 8 == KCHUNKS * NTHREADS, "K staging must cover the tile");
-    static_assert(VKGROUPS * (DV / 8) == NTHREADS, "V staging must cover the tile");
+    static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[DV * VROW];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,68 +108,47 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // ---- staging registers: PF tiles of K/V in flight (loads of tile t+PF are issued while
-    //      tile t is computed)
-    u32x4 kreg[PF][KCHUNKS];
-    u32x4 vreg[PF][VKEYS];
-    const int vkg = tid % VKGROUPS;   // key group (VKEYS consecutive keys)
-    const int vcg = tid / VKGROUPS;   // 8-channel group
-
-    // Per-thread byte offsets inside a tile (constant over the loop).  Each tile gets its own
-    // buffer resource starting at its first key and clamped to the slice end, so keys past sk
-    // (rows are disjoint: stride.s >= d, checked on the host) read as zero with no per-key test.
-    uint32_t koff[KCHUNKS];
+    // ---- K/V tiles go global -> LDS by DMA (buffer_load ... lds): lane l of a wave writes
+    //      16 bytes at block base + 16*l, and its global address decides what lands there.
+    //      K rows keep 16-byte chunk c of row r at chunk c ^ (r % 8); V rows keep chunk c of
+    //      key r at c ^ 2*(r % 4).  Both make the fragment reads below bank-conflict free.
+    //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
+    //      based at the tile and bounded by the slice, so keys past sk land as zeros.
+    uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
-        const int chunk = tid + NTHREADS * i;
-        koff[i] = static_cast<uint32_t>((chunk / (DQK / 8)) * p.kv.ss * 2 + (chunk % (DQK / 8)) * 16);
+    for (int i = 0; i < KDMA; ++i) {
+        const int pos = (wave * KDMA + i) * 1024 + lane * 16;
+        const int r = pos / KROWB, pc = (pos % KROWB) / 16;
+        kgo[i] = static_cast<uint32_t>(r * p.kv.ss * 2 + ((pc ^ (r & 7)) * 16));
     }
-    uint32_t voff[VKEYS];
 #pragma unroll
-    for (int i = 0; i < VKEYS; ++i) voff[i] = static_cast<uint32_t>((vkg * VKEYS + i) * p.vv.ss * 2 + vcg * 16);
-
+    for (int i = 0; i < VDMA; ++i) {
+        const int pos = (wave * VDMA + i) * 1024 + lane * 16;
+        const int r = pos / VROWB, pc = (pos % VROWB) / 16;
+        vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ ((r & 3) << 1)) * 16));
+    }
     auto tile_rsrc = [&](const char* base, const View& vw, int t) __attribute__((always_inline)) {
         const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
         const uint32_t left = start < static_cast<int64_t>(vw.slice_bytes)
                                   ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
-    auto load_tile = [&](int t, auto slot_c) __attribute__((always_inline)) {
-        constexpr int slot = decltype(slot_c)::value;
+    auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
         const auto kr = tile_rsrc(kbase, p.kv, t);
         const auto vr = tile_rsrc(vbase, p.vv, t);
+        uint8_t* kd = lds + stage * STAGE + wave * KDMA * 1024;
+        uint8_t* vd = lds + stage * STAGE + KTILE + wave * VDMA * 1024;
 #pragma unroll
-        for (int i = 0; i < KCHUNKS; ++i) kreg[slot][i] = buffer_load_b128(kr, koff[i]);
+        for (int i = 0; i < KDMA; ++i)
+            buffer_load_lds_b128(kr, kd + i * 1024, kgo[i]);
 #pragma unroll
-        for (int i = 0; i < VKEYS; ++i) vreg[slot][i] = buffer_load_b128(vr, voff[i]);
+        for (int i = 0; i < VDMA; ++i)
+            buffer_load_lds_b128(vr, vd + i * 1024, vgo[i]);
     };
-    auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int slot = decltype(slot_c)::value;
-#pragma unroll
-        for (int i = 0; i < KCHUNKS; ++i) {
-            const int chunk = tid + NTHREADS * i;
-            *reinterpret_cast<u32x4*>(&k_lds[(chunk / (DQK / 8)) * KROW + (chunk % (DQK / 8)) * 8]) = kreg[slot][i];
-        }
-        // V^T: channel (vcg*8 + e) row receives keys vkg*VKEYS .. +VKEYS
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dw = e >> 1;
-            const bool hi = e & 1;
-            uint32_t w[VKEYS / 2];
-#pragma unroll
-            for (int i = 0; i < VKEYS / 2; ++i) {
-                const uint32_t a = vreg[slot][2 * i][dw];
-                const uint32_t c2 = vreg[slot][2 * i + 1][dw];
-                w[i] = hi ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
-            }
-            uint16_t* dst = &v_lds[(vcg * 8 + e) * VROW + vkg * VKEYS];
-            if constexpr (VKEYS == 4) {
-                *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = w[0];
-            }
-        }
-    };
+
+    // LDS starts as zeros so that any row the DMA does not fill holds finite values
+    for (int i = tid; i < 2 * STAGE / 16; i += NTHREADS) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0, 0, 0, 0};
+    __syncthreads();
 
     f32x16 oacc[CBLK];
 #pragma unroll
@@ -179,27 +156,41 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
-    auto compute_tile = [&](int t) __attribute__((always_inline)) {
-        // ---- S^T = K Q^T: two independent 32-key accumulators.  K fragments are read
-        //      KAHEAD k-steps ahead of the MFMAs that use them; the scheduling fences keep
-        //      the compiler from sinking the reads next to their use.
+    // fragment addresses inside a stage (bytes)
+    const int krd0 = col * KROWB;                 // key block 0 row of this lane
+    const int krd1 = (32 + col) * KROWB;          // key block 1 row
+    const int kx = col & 7;                       // the row's chunk swizzle (same for both blocks)
+    const int t16 = lane & 15;
+    // V transposing reads: lane t of a 16-lane group points at key (k0 + t/4), channel
+    // (c0 + 4*(t%4)); the group then receives, lane by lane, 16 consecutive channels of 4 keys.
+    const int vkey_l = half * 4 + (t16 >> 2);                 // key offset inside a 16-key step
+    const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3); // channel offset inside a 32-block
+
+    auto compute_tile = [&](int t, int stage) __attribute__((always_inline)) {
+        const uint8_t* kl = lds + stage * STAGE;
+        const uint8_t* vl = kl + KTILE;
+
+        // ---- S^T = K Q^T: two independent 32-key accumulators; K fragments are read KAHEAD
+        //      k-steps ahead of the MFMAs that use them
         f32x16 s[2] = {f32x16{}, f32x16{}};
         {
             constexpr int KAHEAD = 3;
-            const uint16_t* krow0 = &k_lds[col * KROW + half * 8];
-            const uint16_t* krow1 = krow0 + 32 * KROW;
+            auto kfrag = [&](int row_off, int kk) __attribute__((always_inline)) {
+                const int chunk = (kk * 2 + half) ^ kx;
+                return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + row_off + chunk * 16));
+            };
             bf16x8 fa[KSTEPS], fb[KSTEPS];
 #pragma unroll
             for (int kk = 0; kk < KAHEAD && kk < KSTEPS; ++kk) {
-                fa[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow0 + kk * 16));
-                fb[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow1 + kk * 16));
+                fa[kk] = kfrag(krd0, kk);
+                fb[kk] = kfrag(krd1, kk);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
                 if (kk + KAHEAD < KSTEPS) {
-                    fa[kk + KAHEAD] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow0 + (kk + KAHEAD) * 16));
-                    fb[kk + KAHEAD] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow1 + (kk + KAHEAD) * 16));
+                    fa[kk + KAHEAD] = kfrag(krd0, kk + KAHEAD);
+                    fb[kk + KAHEAD] = kfrag(krd1, kk + KAHEAD);
                 }
                 s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], qf[kk], s[0], 0, 0, 0);
                 s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], qf[kk], s[1], 0, 0, 0);
@@ -260,15 +251,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
             pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
 
-        // ---- O^T += V^T P^T: per 16-key step, CBLK independent accumulators; the V
-        //      fragments of step ks+1 are read while the MFMAs of step ks run
+        // ---- O^T += V^T P^T: the A operand (32 channels x 16 keys) comes from two transposing
+        //      reads of row-major V; keys ks*16 + {half*4 .. +3} and {8 + half*4 .. +3} match
+        //      the key order of P^T's B operand.  Fragments of step ks+1 are read during step ks.
         {
-            const uint16_t* vrow = &v_lds[col * VROW + half * 4];
             auto vfrag = [&](int cb, int ks) __attribute__((always_inline)) {
-                const uint16_t* vr = vrow + cb * 32 * VROW + ks * 16;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-                return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                u32x2 part[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int key = ks * 16 + r * 8 + vkey_l;
+                    const int ch = cb * 32 + vch_l;
+                    const int chunk = (ch >> 3) ^ ((key & 3) << 1);
+                    const uint8_t* a = vl + key * VROWB + chunk * 16 + (ch & 7) * 2;
+                    part[r] = lds_read_tr16_b64(a);
+                }
+                return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
             };
             bf16x8 a[2][CBLK];
 #pragma unroll
@@ -288,23 +285,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         }
     };
 
-    // tiles past the last one load nothing (their buffer range is empty)
-    load_tile(0, std::integral_constant<int, 0>{});
-    if constexpr (PF > 1) load_tile(1, std::integral_constant<int, 1>{});
-    for (int t0 = 0; t0 < ntiles; t0 += PF) {
-        auto step = [&](auto slot_c) __attribute__((always_inline)) {
-            constexpr int slot = decltype(slot_c)::value;
-            const int t = t0 + slot;
-            if (t < ntiles) {
-                __syncthreads();
-                store_tile(slot_c);
-                __syncthreads();
-                load_tile(t + PF, slot_c);
-                compute_tile(t);
-            }
-        };
-        step(std::integral_constant<int, 0>{});
-        if constexpr (PF > 1) step(std::integral_constant<int, 1>{});
+    // ---- main loop: tile t+1 streams into the other stage while tile t is computed; one
+    //      barrier per tile (it also guarantees every wave finished reading the stage that
+    //      the next DMA overwrites)
+    if (ntiles > 0) issue_tile(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile t has landed
+        __syncthreads();
+        issue_tile(t + 1, (t + 1) & 1);       // past the last tile: empty range, nothing read
+        compute_tile(t, t & 1);
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE

@@ -42,6 +42,21 @@ __device__ __forceinline__ uint16_t buffer_load_b16(__amdgpu_buffer_rsrc_t r, ui
     return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l's
+// bytes land at lds + 16*l; `lds` must be the same for the whole wave.  Out-of-range lanes
+// read zeros like any buffer load.
+__device__ __forceinline__ void buffer_load_lds_b128(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): inside each group of 16 lanes, lane t receives
+// element t % 4 of the 8-byte rows addressed by lanes t/4, t/4 + 4, t/4 + 8 and t/4 + 12.
+__device__ __forceinline__ u32x2 lds_read_tr16_b64(const void* lds) {
+    typedef short short4_v __attribute__((__vector_size__(4 * sizeof(short))));
+    const auto pa = (__attribute__((address_space(3))) short4_v*)(const_cast<void*>(lds));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa));
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }

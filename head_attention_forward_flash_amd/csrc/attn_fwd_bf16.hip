@@ -45,12 +45,21 @@ namespace mha {
 namespace {
 
 constexpr int BM = 128;       // query rows per workgroup
-constexpr int BN = 64;        // keys per tile
 constexpr int NTHREADS = 256;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
+// Tile shape per head-dim pair: BN keys per tile, NSTAGE tiles in the LDS ring (NSTAGE - 1
+// of them in flight while one is computed); two workgroups share a CU's 160 KiB of LDS.
+template <int DQK, int DV> struct TileCfg;
+template <> struct TileCfg<64, 64> { static constexpr int BN = 64, NSTAGE = 2; };
+template <> struct TileCfg<128, 128> { static constexpr int BN = 64, NSTAGE = 2; };
+template <> struct TileCfg<192, 128> { static constexpr int BN = 64, NSTAGE = 2; };
+
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
+    constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
+    constexpr int NSTAGE = TileCfg<DQK, DV>::NSTAGE;
+    constexpr int KB = BN / 32;                        // 32-key blocks per tile
     constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
     constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
     constexpr int KTILE = BN * KROWB;
@@ -62,7 +71,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     constexpr int CBLK = DV / 32;             // 32-channel output blocks
     static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+    static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per CU must fit in LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,22 +120,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 
     // ---- K/V tiles go global -> LDS by DMA (buffer_load ... lds): lane l of a wave writes
     //      16 bytes at block base + 16*l, and its global address decides what lands there.
-    //      K rows keep 16-byte chunk c of row r at chunk c ^ (r % 8); V rows keep chunk c of
-    //      key r at c ^ 2*(r % 4).  Both make the fragment reads below bank-conflict free.
+    //      Rows are unpadded and their 16-byte chunks XOR-swizzled so that the fragment reads
+    //      below are bank-conflict free on gfx950's LDS, which serves 256 bytes per clock
+    //      (16 lanes of a b128 read, 32 lanes of a b64 read):
+    //        K: the 16 rows one b128 read touches land on 16 distinct 16-byte bank groups;
+    //        V: the 4 rows one transposing read touches land on 4 distinct 64-byte quarters.
     //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
     //      based at the tile and bounded by the slice, so keys past sk land as zeros.
+    auto kswz = [](int r) __attribute__((always_inline)) {
+        return KROWB % 256 == 0 ? (r & 15) : ((r >> 1) & 7);    // rows of 256 B, else 128/384 B
+    };
+    auto vswz = [](int r) __attribute__((always_inline)) {
+        return VROWB % 256 == 0 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+    };
     uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
     for (int i = 0; i < KDMA; ++i) {
         const int pos = (wave * KDMA + i) * 1024 + lane * 16;
         const int r = pos / KROWB, pc = (pos % KROWB) / 16;
-        kgo[i] = static_cast<uint32_t>(r * p.kv.ss * 2 + ((pc ^ (r & 7)) * 16));
+        kgo[i] = static_cast<uint32_t>(r * p.kv.ss * 2 + ((pc ^ kswz(r)) * 16));
     }
 #pragma unroll
     for (int i = 0; i < VDMA; ++i) {
         const int pos = (wave * VDMA + i) * 1024 + lane * 16;
         const int r = pos / VROWB, pc = (pos % VROWB) / 16;
-        vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ ((r & 3) << 1)) * 16));
+        vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
     }
     auto tile_rsrc = [&](const char* base, const View& vw, int t) __attribute__((always_inline)) {
         const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
@@ -147,7 +166,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     };
 
     // LDS starts as zeros so that any row the DMA does not fill holds finite values
-    for (int i = tid; i < 2 * STAGE / 16; i += NTHREADS) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < NSTAGE * STAGE / 16; i += NTHREADS) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0, 0, 0, 0};
     __syncthreads();
 
     f32x16 oacc[CBLK];
@@ -157,9 +176,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
     // fragment addresses inside a stage (bytes)
-    const int krd0 = col * KROWB;                 // key block 0 row of this lane
-    const int krd1 = (32 + col) * KROWB;          // key block 1 row
-    const int kx = col & 7;                       // the row's chunk swizzle (same for both blocks)
+    const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
     const int t16 = lane & 15;
     // V transposing reads: lane t of a 16-lane group points at key (k0 + t/4), channel
     // (c0 + 4*(t%4)); the group then receives, lane by lane, 16 consecutive channels of 4 keys.
@@ -170,30 +187,32 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         const uint8_t* kl = lds + stage * STAGE;
         const uint8_t* vl = kl + KTILE;
 
-        // ---- S^T = K Q^T: two independent 32-key accumulators; K fragments are read KAHEAD
+        // ---- S^T = K Q^T: KB independent 32-key accumulators; K fragments are read KAHEAD
         //      k-steps ahead of the MFMAs that use them
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+        f32x16 s[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
         {
             constexpr int KAHEAD = 3;
-            auto kfrag = [&](int row_off, int kk) __attribute__((always_inline)) {
+            auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
                 const int chunk = (kk * 2 + half) ^ kx;
-                return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + row_off + chunk * 16));
+                return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + (kb * 32 + col) * KROWB + chunk * 16));
             };
-            bf16x8 fa[KSTEPS], fb[KSTEPS];
+            bf16x8 fr[KSTEPS][KB];
 #pragma unroll
-            for (int kk = 0; kk < KAHEAD && kk < KSTEPS; ++kk) {
-                fa[kk] = kfrag(krd0, kk);
-                fb[kk] = kfrag(krd1, kk);
-            }
+            for (int kk = 0; kk < KAHEAD && kk < KSTEPS; ++kk)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) fr[kk][kb] = kfrag(kb, kk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
                 if (kk + KAHEAD < KSTEPS) {
-                    fa[kk + KAHEAD] = kfrag(krd0, kk + KAHEAD);
-                    fb[kk + KAHEAD] = kfrag(krd1, kk + KAHEAD);
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) fr[kk + KAHEAD][kb] = kfrag(kb, kk + KAHEAD);
                 }
-                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], qf[kk], s[0], 0, 0, 0);
-                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], qf[kk], s[1], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk][kb], qf[kk], s[kb], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         const bool need_mask = (key0 + BN > p.sk) || (CAUSAL && key0 + BN - 1 > wave_row0);
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = key0 + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
@@ -215,7 +234,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 #pragma unroll
         for (int j = 2; j < 16; j += 2) mt = max3(mt, s[0][j], s[0][j + 1]);
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) mt = max3(mt, s[1][j], s[1][j + 1]);
+        for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) mt = max3(mt, s[kb][j], s[kb][j + 1]);
         mt = fmaxf(mt, swap_halves(mt));
 
         // ---- online softmax with lazy rescaling (the reference max only moves when a row's
@@ -231,9 +252,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         }
         const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
 
-        bf16x8 pf[4];
+        constexpr int PSTEPS = BN / 16;   // 16-key MFMA steps of P.V
+        bf16x8 pf[PSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < PSTEPS; ++ks) {
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -261,7 +283,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
                 for (int r = 0; r < 2; ++r) {
                     const int key = ks * 16 + r * 8 + vkey_l;
                     const int ch = cb * 32 + vch_l;
-                    const int chunk = (ch >> 3) ^ ((key & 3) << 1);
+                    const int chunk = (ch >> 3) ^ vswz(key);
                     const uint8_t* a = vl + key * VROWB + chunk * 16 + (ch & 7) * 2;
                     part[r] = lds_read_tr16_b64(a);
                 }
@@ -272,8 +294,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
             for (int cb = 0; cb < CBLK; ++cb) a[0][cb] = vfrag(cb, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks + 1 < 4) {
+            for (int ks = 0; ks < PSTEPS; ++ks) {
+                if (ks + 1 < PSTEPS) {
 #pragma unroll
                     for (int cb = 0; cb < CBLK; ++cb) a[(ks + 1) & 1][cb] = vfrag(cb, ks + 1);
                 }
@@ -285,15 +307,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         }
     };
 
-    // ---- main loop: tile t+1 streams into the other stage while tile t is computed; one
-    //      barrier per tile (it also guarantees every wave finished reading the stage that
-    //      the next DMA overwrites)
-    if (ntiles > 0) issue_tile(0, 0);
+    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed.  The
+    //      barrier makes every wave's part of tile t visible and guarantees that every wave
+    //      finished tile t - 1, whose stage the next DMA overwrites.
+    constexpr int DMA_PER_TILE = KDMA + VDMA;
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) issue_tile(i, i);   // tiles past the end read nothing
+    int stage = 0;
     for (int t = 0; t < ntiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile t has landed
+        // wait until at most the DMAs of the NSTAGE - 2 younger tiles are outstanding
+        static_assert((NSTAGE - 2) * DMA_PER_TILE < 64, "vmcnt is 6 bits");
+        constexpr int vm = (NSTAGE - 2) * DMA_PER_TILE;
+        __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x0F70);
         __syncthreads();
-        issue_tile(t + 1, (t + 1) & 1);       // past the last tile: empty range, nothing read
-        compute_tile(t, t & 1);
+        const int ahead = stage == 0 ? NSTAGE - 1 : stage - 1;   // (t + NSTAGE - 1) % NSTAGE
+        issue_tile(t + NSTAGE - 1, ahead);
+        compute_tile(t, stage);
+        stage = stage + 1 == NSTAGE ? 0 : stage + 1;
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE

@@ -72,7 +72,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
 
     static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per CU must fit in LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+    // Two stages as two distinct LDS objects: the compiler's wait insertion then knows that the
+    // DMA filling one stage cannot alias the fragment reads of the other, and does not make
+    // the computation of tile t wait for the loads of tile t+1.
+    static_assert(NSTAGE == 2, "the ring is two named stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -152,11 +157,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
                                   ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
-    auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    auto issue_tile = [&](int t, uint8_t* stage_base) __attribute__((always_inline)) {
         const auto kr = tile_rsrc(kbase, p.kv, t);
         const auto vr = tile_rsrc(vbase, p.vv, t);
-        uint8_t* kd = lds + stage * STAGE + wave * KDMA * 1024;
-        uint8_t* vd = lds + stage * STAGE + KTILE + wave * VDMA * 1024;
+        uint8_t* kd = stage_base + wave * KDMA * 1024;
+        uint8_t* vd = stage_base + KTILE + wave * VDMA * 1024;
 #pragma unroll
         for (int i = 0; i < KDMA; ++i)
             buffer_load_lds_b128(kr, kd + i * 1024, kgo[i]);
@@ -166,7 +171,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     };
 
     // LDS starts as zeros so that any row the DMA does not fill holds finite values
-    for (int i = tid; i < NSTAGE * STAGE / 16; i += NTHREADS) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < STAGE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(lds1)[i] = u32x4{0, 0, 0, 0};
+    }
     __syncthreads();
 
     f32x16 oacc[CBLK];
@@ -183,8 +191,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     const int vkey_l = half * 4 + (t16 >> 2);                 // key offset inside a 16-key step
     const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3); // channel offset inside a 32-block
 
-    auto compute_tile = [&](int t, int stage) __attribute__((always_inline)) {
-        const uint8_t* kl = lds + stage * STAGE;
+    auto compute_tile = [&](int t, const uint8_t* kl) __attribute__((always_inline)) {
         const uint8_t* vl = kl + KTILE;
 
         // ---- S^T = K Q^T: KB independent 32-key accumulators; K fragments are read KAHEAD
@@ -307,23 +314,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         }
     };
 
-    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed.  The
-    //      barrier makes every wave's part of tile t visible and guarantees that every wave
-    //      finished tile t - 1, whose stage the next DMA overwrites.
-    constexpr int DMA_PER_TILE = KDMA + VDMA;
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i) issue_tile(i, i);   // tiles past the end read nothing
-    int stage = 0;
-    for (int t = 0; t < ntiles; ++t) {
-        // wait until at most the DMAs of the NSTAGE - 2 younger tiles are outstanding
-        static_assert((NSTAGE - 2) * DMA_PER_TILE < 64, "vmcnt is 6 bits");
-        constexpr int vm = (NSTAGE - 2) * DMA_PER_TILE;
-        __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x0F70);
+    // ---- main loop: tile t+1 streams into one stage while tile t is computed from the other.
+    //      The barrier makes every wave's part of tile t visible and guarantees that every
+    //      wave finished tile t - 1, whose stage the next DMA overwrites.
+    auto step = [&](int t, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile t has landed
         __syncthreads();
-        const int ahead = stage == 0 ? NSTAGE - 1 : stage - 1;   // (t + NSTAGE - 1) % NSTAGE
-        issue_tile(t + NSTAGE - 1, ahead);
-        compute_tile(t, stage);
-        stage = stage + 1 == NSTAGE ? 0 : stage + 1;
+        issue_tile(t + 1, nxt);               // past the last tile: empty range, nothing read
+        compute_tile(t, cur);
+    };
+    issue_tile(0, lds0);
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, lds0, lds1);
+        if (t + 1 < ntiles) step(t + 1, lds1, lds0);
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE

@@ -44,19 +44,23 @@
 namespace mha {
 namespace {
 
-constexpr int BM = 128;       // query rows per workgroup
-constexpr int NTHREADS = 256;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-// Tile shape per head-dim pair: BN keys per tile, NSTAGE tiles in the LDS ring (NSTAGE - 1
-// of them in flight while one is computed); two workgroups share a CU's 160 KiB of LDS.
+// Tile shape per head-dim pair: BM query rows per workgroup (32 per wave), BN keys per tile,
+// NSTAGE tiles in the LDS ring (NSTAGE - 1 in flight while one is computed).  128-row
+// workgroups run two per CU (80 KiB of LDS each); the 256-row one runs alone with 8 waves.
+// Chosen by A/B timing on MI355X: 256 rows halve the K/V traffic per FLOP, which pays off
+// for the wide d192/d128 tiles; three stages help only the short d64 tiles.
 template <int DQK, int DV> struct TileCfg;
-template <> struct TileCfg<64, 64> { static constexpr int BN = 64, NSTAGE = 2; };
-template <> struct TileCfg<128, 128> { static constexpr int BN = 64, NSTAGE = 2; };
-template <> struct TileCfg<192, 128> { static constexpr int BN = 64, NSTAGE = 2; };
+template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, NSTAGE = 3; };
+template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, NSTAGE = 2; };
+template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, NSTAGE = 2; };
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
+__global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
+    constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
+    constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
+    constexpr int NWAVES = NTHREADS / 64;
     constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
     constexpr int NSTAGE = TileCfg<DQK, DV>::NSTAGE;
     constexpr int KB = BN / 32;                        // 32-key blocks per tile
@@ -65,19 +69,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     constexpr int KTILE = BN * KROWB;
     constexpr int VTILE = BN * VROWB;
     constexpr int STAGE = KTILE + VTILE;      // one LDS stage: a K tile then a V tile
-    constexpr int KDMA = KTILE / 1024 / 4;    // 1 KiB DMA blocks per wave per K tile
-    constexpr int VDMA = VTILE / 1024 / 4;
+    constexpr int KDMA = KTILE / 1024 / NWAVES;   // 1 KiB DMA blocks per wave per K tile
+    constexpr int VDMA = VTILE / 1024 / NWAVES;
     constexpr int KSTEPS = DQK / 16;          // MFMA k-steps for S^T
     constexpr int CBLK = DV / 32;             // 32-channel output blocks
-    static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
+    static_assert(KDMA * NWAVES * 1024 == KTILE && VDMA * NWAVES * 1024 == VTILE, "DMA blocks must cover the tiles");
 
-    static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per CU must fit in LDS");
-    // Two stages as two distinct LDS objects: the compiler's wait insertion then knows that the
-    // DMA filling one stage cannot alias the fragment reads of the other, and does not make
-    // the computation of tile t wait for the loads of tile t+1.
-    static_assert(NSTAGE == 2, "the ring is two named stages");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring of 2 to 4 stages");
+    static_assert(NSTAGE * STAGE <= (BM == 128 ? 80 : 160) * 1024, "the workgroups of a CU must fit in LDS");
+    // The stages are distinct LDS objects: the compiler's wait insertion then knows that the
+    // DMA filling one stage cannot alias the fragment reads of another, and does not make the
+    // computation of tile t wait for the loads of later tiles.
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NSTAGE > 2 ? STAGE : 1024];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NSTAGE > 3 ? STAGE : 1024];
+    auto stage_ptr = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int i = decltype(i_c)::value % NSTAGE;
+        if constexpr (i == 0) return lds0;
+        else if constexpr (i == 1) return lds1;
+        else if constexpr (i == 2) return lds2;
+        else return lds3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,6 +187,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
     for (int i = tid; i < STAGE / 16; i += NTHREADS) {
         reinterpret_cast<u32x4*>(lds0)[i] = u32x4{0, 0, 0, 0};
         reinterpret_cast<u32x4*>(lds1)[i] = u32x4{0, 0, 0, 0};
+        if constexpr (NSTAGE > 2) reinterpret_cast<u32x4*>(lds2)[i] = u32x4{0, 0, 0, 0};
+        if constexpr (NSTAGE > 3) reinterpret_cast<u32x4*>(lds3)[i] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
 
@@ -314,19 +329,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
         }
     };
 
-    // ---- main loop: tile t+1 streams into one stage while tile t is computed from the other.
-    //      The barrier makes every wave's part of tile t visible and guarantees that every
-    //      wave finished tile t - 1, whose stage the next DMA overwrites.
-    auto step = [&](int t, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile t has landed
-        __syncthreads();
-        issue_tile(t + 1, nxt);               // past the last tile: empty range, nothing read
-        compute_tile(t, cur);
+    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed.  The
+    //      barrier makes every wave's part of tile t visible and guarantees that every wave
+    //      finished tile t - 1, whose stage the next DMA overwrites.
+    constexpr int DMA_PER_TILE = KDMA + VDMA;
+    constexpr int VM_LEFT = (NSTAGE - 2) * DMA_PER_TILE;   // DMAs of younger tiles still in flight
+    static_assert(VM_LEFT < 64, "vmcnt is 6 bits");
+    constexpr int WAIT_TILE = (VM_LEFT & 15) | ((VM_LEFT >> 4) << 14) | 0x0F70;   // vmcnt(VM_LEFT)
+    auto prologue = [&](auto i_c) __attribute__((always_inline)) {
+        if constexpr (decltype(i_c)::value < NSTAGE - 1) issue_tile(decltype(i_c)::value, stage_ptr(i_c));
     };
-    issue_tile(0, lds0);
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, lds0, lds1);
-        if (t + 1 < ntiles) step(t + 1, lds1, lds0);
+    prologue(std::integral_constant<int, 0>{});
+    prologue(std::integral_constant<int, 1>{});
+    prologue(std::integral_constant<int, 2>{});
+    for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
+        auto step = [&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            const int t = t0 + j;
+            if (j < NSTAGE && t < ntiles) {
+                __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // this wave's part of tile t has landed
+                __syncthreads();
+                // past the last tile: empty buffer range, nothing is read
+                issue_tile(t + NSTAGE - 1, stage_ptr(std::integral_constant<int, j + NSTAGE - 1>{}));
+                compute_tile(t, stage_ptr(j_c));
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        if constexpr (NSTAGE > 2) step(std::integral_constant<int, 2>{});
+        if constexpr (NSTAGE > 3) step(std::integral_constant<int, 3>{});
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE
@@ -352,16 +383,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_bf16_kernel(const AttnPa
 }
 
 template <int DQK, int DV, bool CAUSAL>
-hipError_t launch(const AttnParams& p, hipStream_t stream) {
+hipError_t launch(AttnParams p, hipStream_t stream) {
+    constexpr int BM = TileCfg<DQK, DV>::BM;
+    p.n_mblocks = (p.sq + BM - 1) / BM;
     const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
+    if (nwg == 0) return hipSuccess;
+    if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(NTHREADS), 0, stream, p);
+                       dim3(BM * 2), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
-
-int attn_fwd_bf16_block_m() { return BM; }
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
     if (d_qk == 64 && d_v == 64) return causal ? launch<64, 64, true>(p, stream) : launch<64, 64, false>(p, stream);

@@ -22,13 +22,12 @@ struct AttnParams {
     View qv, kv, vv, ov;
     int b, hq, hk, sq, sk;
     int group;       // hq / hk
-    int n_mblocks;   // ceil(sq / BLOCK_M)
+    int n_mblocks;   // ceil(sq / rows per workgroup), set by the launcher
     float scale_log2;  // softmax_scale * log2(e)
 };
 
 // bf16 attention forward: d_qk/d_v in {(64,64), (128,128), (192,128)}.
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream);
-int attn_fwd_bf16_block_m();
 
 struct GateParams {
     const void* k;

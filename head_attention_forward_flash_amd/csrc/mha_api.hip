@@ -139,9 +139,8 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
     if (sk > 1 && v_stride.s < d_v)
         return fail(MHA_ERR_LAYOUT, "v: rows overlap (stride.s = %lld < d_v = %d)", (long long)v_stride.s, d_v);
 
-    const int bm = mha::attn_fwd_bf16_block_m();
-    const int n_mblocks = (sq + bm - 1) / bm;
-    const int64_t nwg = int64_t(b) * hq * n_mblocks;
+    // the launcher sizes the grid from its tile configuration (at least 128 rows per workgroup)
+    const int64_t nwg = int64_t(b) * hq * ((int64_t(sq) + 127) / 128);
     if (nwg > INT32_MAX) return fail(MHA_ERR_OVERFLOW, "grid of %lld workgroups exceeds 2^31-1", (long long)nwg);
     if (nwg == 0) return ok();
 
@@ -156,7 +155,6 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
     p.sq = sq;
     p.sk = sk;
     p.group = hq / hk;
-    p.n_mblocks = n_mblocks;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
     return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
                       "attn_fwd_bf16 launch");

@@ -164,7 +164,7 @@ def mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d) -> int:
 
 
 def mha_fp8_workspace_layout(b, hq, hk, sq, sk, d):
-    """Byte offsets of (q codes, k codes, v codes, q scales, k scales, v scales) in the fp8 workspace."""
+    """Byte offsets of (q codes, k codes, v values as bf16, q scales, k scales, v scales) in the fp8 workspace."""
     lib = load_library()
     arr = (ctypes.c_size_t * 6)()
     _check(lib.mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, arr))

@@ -2,11 +2,12 @@
 //
 // The attention side of the FP8 hd128 mha_v4 recipe ("[HIP] Mha v4: run the
 // K-smoothing gate as one HIP call", Performance table; "MHA v4: fixes,
-// refactor, new kernel, perf tweaks", BF16/FP8 recipe).  Inputs are the codes
-// and per-(batch, head, 128-token block) fp32 scales written by quant_fp8.
+// refactor, new kernel, perf tweaks", BF16/FP8 recipe).  Inputs are written by
+// quant_fp8: E4M3 codes of Q and K - mean, the E4M3 values of V widened exactly
+// to bf16, and one fp32 scale per (batch, head, 128-token block) for each.
 //
-// Same decomposition as the bf16 kernel (4 waves x 32 query rows, 64-key
-// tiles, one query per lane in S^T), with:
+// Same pipeline as the bf16 kernel (4 waves x 32 query rows, 64-key tiles, one
+// query per lane in S^T, K/V tiles staged into a ring of LDS stages by DMA):
 //   S^T = K8 Q8^T  on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate),
 //                  two k-steps of 64 channels; both operands read 32 bytes of
 //                  their row per lane, so the MFMA's channel order cancels out;
@@ -14,12 +15,12 @@
 //                  factor per tile, since a 64-key tile sits inside one
 //                  128-token scale block and the 128 query rows are one block;
 //                  the factor and the running max fold into one FMA before exp2;
-//   P.V            on bf16 MFMA: V codes are widened exactly to bf16 while the
-//                  tile is staged (transposed) into LDS, and the V block scale
-//                  enters P through the exponent (p' = exp2(t - m + log2 scale_v))
-//                  before P is rounded to bf16;
+//   P.V            on bf16 MFMA; the V operand comes from transposing LDS reads of
+//                  the widened V values, and the V block scale enters P through
+//                  the exponent (p' = exp2(t - m + log2 scale_v)) before P is
+//                  rounded to bf16;
 //   l              sums the bf16 P' fed to P.V (v_dot2_f32_bf16), divided by the
-//                  tile's V scale once per tile; two tiles of codes are in flight.
+//                  tile's V scale once per tile.
 
 #include <type_traits>
 
@@ -29,30 +30,37 @@
 namespace mha {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 64;
+constexpr int BM = 128;          // query rows per workgroup = one Q scale block
+constexpr int BN = 64;           // keys per tile (half a K/V scale block)
 constexpr int D = 128;
 constexpr int NTHREADS = 256;
+constexpr int NSTAGE = 3;
 constexpr float kRescaleThreshold = 8.0f;
-
-__device__ __forceinline__ u32x2 buffer_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
-
-// 4 E4M3 codes (one dword) -> 4 bf16 values in two dwords (exact widening).
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-    return u32x2{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(hi[0], hi[1])};
-}
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
-    constexpr int KROW = D + 16;          // bytes per K8 row in LDS
-    constexpr int VROW = BN + 4;          // bf16 elements per V^T row in LDS
+    constexpr int KROWB = D;                  // bytes per K8 row
+    constexpr int VROWB = D * 2;              // bytes per widened V row
+    constexpr int KTILE = BN * KROWB;
+    constexpr int VTILE = BN * VROWB;
+    constexpr int STAGE = KTILE + VTILE;
+    constexpr int KDMA = KTILE / 1024 / 4;    // 1 KiB DMA blocks per wave per tile
+    constexpr int VDMA = VTILE / 1024 / 4;
     constexpr int CBLK = D / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[BN * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VROW];
+    static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
+    static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per CU must fit in LDS");
+
+    // distinct LDS objects per stage (see the bf16 kernel: keeps the DMA of later tiles from
+    // gating the fragment reads of the current one)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGE];
+    auto stage_ptr = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int i = decltype(i_c)::value % NSTAGE;
+        if constexpr (i == 0) return lds0;
+        else if constexpr (i == 1) return lds1;
+        else return lds2;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -73,8 +81,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const int bg = bb * p.hk + g;
 
     const uint32_t qslice = static_cast<uint32_t>(p.nq) * BM * D;
-    const uint32_t kslice = static_cast<uint32_t>(p.nk) * BM * D;
+    const uint32_t kslice = static_cast<uint32_t>(p.nk) * BM * KROWB;
+    const uint32_t vslice = static_cast<uint32_t>(p.nk) * BM * VROWB;
     const auto qrs = make_rsrc(p.q + static_cast<int64_t>(bh) * qslice, qslice);
+    const uint8_t* kbase = p.k + static_cast<int64_t>(bg) * kslice;
+    const uint8_t* vbase = p.v + static_cast<int64_t>(bg) * vslice;
     const float q_scale = p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
     const float* k_scale = p.k_scale + static_cast<int64_t>(bg) * p.nk;
     const float* v_scale = p.v_scale + static_cast<int64_t>(bg) * p.nk;
@@ -98,64 +109,46 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // two tiles of codes in flight (loads of tile t+2 are issued while tile t is computed)
-    constexpr int PF = 2;
-    u32x4 kreg[PF][2];
-    u32x2 vreg[PF][4];
-    const int vkg = tid % 16;   // 4 keys
-    const int vcg = tid / 16;   // 8 channels
-    uint32_t koff[2];
+    // ---- DMA layout (see the bf16 kernel): K8 rows of 128 B keep chunk c of row r at
+    //      c ^ ((r >> 1) & 7); widened V rows of 256 B keep chunk c of key r at c ^ 4*(r & 3).
+    auto kswz = [](int r) __attribute__((always_inline)) { return (r >> 1) & 7; };
+    auto vswz = [](int r) __attribute__((always_inline)) { return (r & 3) << 2; };
+    uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int chunk = tid + NTHREADS * i;
-        koff[i] = static_cast<uint32_t>((chunk / (D / 16)) * D + (chunk % (D / 16)) * 16);
+    for (int i = 0; i < KDMA; ++i) {
+        const int pos = (wave * KDMA + i) * 1024 + lane * 16;
+        const int r = pos / KROWB, pc = (pos % KROWB) / 16;
+        kgo[i] = static_cast<uint32_t>(r * KROWB + (pc ^ kswz(r)) * 16);
     }
-    uint32_t voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = static_cast<uint32_t>((vkg * 4 + i) * D + vcg * 8);
-
-    auto load_tile = [&](int t, auto slot_c) __attribute__((always_inline)) {
-        constexpr int slot = decltype(slot_c)::value;
+    for (int i = 0; i < VDMA; ++i) {
+        const int pos = (wave * VDMA + i) * 1024 + lane * 16;
+        const int r = pos / VROWB, pc = (pos % VROWB) / 16;
+        vgo[i] = static_cast<uint32_t>(r * VROWB + (pc ^ vswz(r)) * 16);
+    }
+    auto tile_rsrc = [&](const uint8_t* base, uint32_t slice, uint32_t rowb, int t) __attribute__((always_inline)) {
+        const uint32_t start = static_cast<uint32_t>(t) * BN * rowb;
+        const uint32_t left = start < slice ? slice - start : 0u;
+        return make_rsrc(left ? base + start : base, left);
+    };
+    auto issue_tile = [&](int t, uint8_t* stage_base) __attribute__((always_inline)) {
         // tiles past the padded key range read nothing (empty buffer range)
-        const uint32_t start = static_cast<uint32_t>(t) * BN * D;
-        const uint32_t left = start < kslice ? kslice - start : 0u;
-        const auto kr = make_rsrc(p.k + static_cast<int64_t>(bg) * kslice + (left ? start : 0), left);
-        const auto vr = make_rsrc(p.v + static_cast<int64_t>(bg) * kslice + (left ? start : 0), left);
+        const auto kr = tile_rsrc(kbase, kslice, KROWB, t);
+        const auto vr = tile_rsrc(vbase, vslice, VROWB, t);
+        uint8_t* kd = stage_base + wave * KDMA * 1024;
+        uint8_t* vd = stage_base + KTILE + wave * VDMA * 1024;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) kreg[slot][i] = buffer_load_b128(kr, koff[i]);
+        for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(kr, kd + i * 1024, kgo[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vreg[slot][i] = buffer_load_b64(vr, voff[i]);
+        for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(vr, vd + i * 1024, vgo[i]);
     };
 
-    auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int slot = decltype(slot_c)::value;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int chunk = tid + NTHREADS * i;
-            *reinterpret_cast<u32x4*>(&k_lds[(chunk / (D / 16)) * KROW + (chunk % (D / 16)) * 16]) = kreg[slot][i];
-        }
-        // widen the 4 keys x 8 channels of V codes to bf16, then write channel rows
-        u32x4 wide[4];   // per key: 8 bf16 = 4 dwords (channel pairs)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x2 a = e4m3x4_to_bf16x4(vreg[slot][i][0]);
-            const u32x2 b = e4m3x4_to_bf16x4(vreg[slot][i][1]);
-            wide[i] = u32x4{a[0], a[1], b[0], b[1]};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dw = e >> 1;
-            const bool hi = e & 1;
-            uint32_t w[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t a = wide[2 * i][dw];
-                const uint32_t c2 = wide[2 * i + 1][dw];
-                w[i] = hi ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
-            }
-            *reinterpret_cast<u32x2*>(&v_lds[(vcg * 8 + e) * VROW + vkg * 4]) = u32x2{w[0], w[1]};
-        }
-    };
+    for (int i = tid; i < STAGE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(lds1)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(lds2)[i] = u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
 
     f32x16 oacc[CBLK];
 #pragma unroll
@@ -163,32 +156,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     float m_run = kNegInf;   // running max in base-2 units of scaled scores
     float l_run = 0.f;
 
-    auto compute_tile = [&](int t) __attribute__((always_inline)) {
+    const int kx = kswz(col);
+    const int t16 = lane & 15;
+    const int vkey_l = half * 4 + (t16 >> 2);
+    const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3);
+
+    auto compute_tile = [&](int t, const uint8_t* kl) __attribute__((always_inline)) {
+        const uint8_t* vl = kl + KTILE;
         const int kblk = (t * BN) / BM;
         const float c = cq * k_scale[kblk];            // this tile's base-2 score factor
         const float log2_sv = __log2f(v_scale[kblk]);  // V block scale, folded into P
         const float inv_sv = 1.f / v_scale[kblk];
 
-        // S^T = K8 Q8^T: two 32-key accumulators, two k-steps of 64 channels
+        // ---- S^T = K8 Q8^T: two 32-key accumulators, two k-steps of 64 channels
         f32x16 s[2] = {f32x16{}, f32x16{}};
         {
-            const uint8_t* krow0 = &k_lds[col * KROW + half * 32];
-            const uint8_t* krow1 = krow0 + 32 * KROW;
-            i32x8 fa[2], fb[2];
+            i32x8 fr[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow0 + ks * 64);
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow0 + ks * 64 + 16);
-                const u32x4 b0 = *reinterpret_cast<const u32x4*>(krow1 + ks * 64);
-                const u32x4 b1 = *reinterpret_cast<const u32x4*>(krow1 + ks * 64 + 16);
-                fa[ks] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                fb[ks] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint8_t* row = kl + (kb * 32 + col) * KROWB;
+                    const int c0 = (ks * 4 + half * 2) ^ kx, c1 = (ks * 4 + half * 2 + 1) ^ kx;
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + c0 * 16);
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + c1 * 16);
+                    fr[ks][kb] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                       (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                s[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ks], qf[ks], s[0], 0, 0, 0, 0, 0, 0);
-                s[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ks], qf[ks], s[1], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[ks][kb], qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
             }
         }
 
@@ -246,13 +247,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         }
         l_run = fmaf(l_tile, inv_sv, l_run);   // back to unscaled probabilities
 
+        // ---- O^T += V^T P'^T from transposing reads of the widened V rows
         {
-            const uint16_t* vrow = &v_lds[col * VROW + half * 4];
             auto vfrag = [&](int cb, int ks) __attribute__((always_inline)) {
-                const uint16_t* vr = vrow + cb * 32 * VROW + ks * 16;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-                return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                u32x2 part[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int key = ks * 16 + r * 8 + vkey_l;
+                    const int ch = cb * 32 + vch_l;
+                    const int chunk = (ch >> 3) ^ vswz(key);
+                    part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
+                }
+                return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
             };
             bf16x8 a[2][CBLK];
 #pragma unroll
@@ -272,22 +278,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         }
     };
 
-    load_tile(0, std::integral_constant<int, 0>{});
-    load_tile(1, std::integral_constant<int, 1>{});
-    for (int t0 = 0; t0 < ntiles; t0 += PF) {
-        auto step = [&](auto slot_c) __attribute__((always_inline)) {
-            constexpr int slot = decltype(slot_c)::value;
-            const int t = t0 + slot;
+    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed
+    constexpr int VM_LEFT = (NSTAGE - 2) * (KDMA + VDMA);
+    static_assert(VM_LEFT < 16, "vmcnt immediate");
+    constexpr int WAIT_TILE = VM_LEFT | 0x0F70;
+    issue_tile(0, lds0);
+    issue_tile(1, lds1);
+    for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
+        auto step = [&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            const int t = t0 + j;
             if (t < ntiles) {
+                __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // this wave's part of tile t has landed
                 __syncthreads();
-                store_tile(slot_c);
-                __syncthreads();
-                load_tile(t + PF, slot_c);
-                compute_tile(t);
+                issue_tile(t + NSTAGE - 1, stage_ptr(std::integral_constant<int, j + NSTAGE - 1>{}));
+                compute_tile(t, stage_ptr(j_c));
             }
         };
         step(std::integral_constant<int, 0>{});
         step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
     }
 
     const float l_tot = l_run + swap_halves(l_run);
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
             }
         }
         if (p.lse != nullptr && half == 0) {
-            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;   // m_run is already scaled
+            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;   // m_run is scaled
             p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
         }
     }

@@ -53,8 +53,9 @@ struct QuantParams {
     const float* mean;  // [b, heads, d] subtracted before quantising, or null
     int b, heads, s, d;
     int nblk;            // ceil(s / 128)
-    uint8_t* codes;      // [b, heads, nblk*128, d]
+    uint8_t* codes;      // [b, heads, nblk*128, d]: E4M3 codes, or with `widen` their values as bf16
     float* scales;       // [b, heads, nblk]
+    bool widen;          // store each code's value widened (exactly) to bf16 instead of the byte
 };
 
 hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const QuantParams& v,

@@ -224,7 +224,7 @@ mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d
     offsets[1] = off;
     off = align256(off + size_t(b) * hk * nk * 128 * d);
     offsets[2] = off;
-    off = align256(off + size_t(b) * hk * nk * 128 * d);
+    off = align256(off + size_t(b) * hk * nk * 128 * d * 2);   // V values widened to bf16
     offsets[3] = off;
     off = align256(off + size_t(b) * hq * nq * 4);
     offsets[4] = off;
@@ -265,7 +265,7 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
     if (b == 0 || sq == 0) return ok();
     const int64_t nq = (int64_t(sq) + 127) / 128, nk = (int64_t(sk) + 127) / 128;
-    if (std::max(nq, nk) * 128 * d >= kMaxSliceBytes)
+    if (std::max(nq, nk) * 128 * d * 2 >= kMaxSliceBytes)
         return fail(MHA_ERR_OVERFLOW, "fp8: one (batch, head) slice of codes spans >= 2^31 bytes");
     const int64_t nwg = int64_t(b) * hq * nq;
     const int64_t nquant = int64_t(b) * (hq * nq + 2 * hk * nk);
@@ -276,7 +276,7 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, off);
     char* wsb = static_cast<char*>(ws);
     auto quant = [&](const void* src, const mha::View& sv, const float* mean, int heads, int s, int64_t nblk,
-                     size_t code_off, size_t scale_off) {
+                     size_t code_off, size_t scale_off, bool widen) {
         mha::QuantParams qp{};
         qp.src = src;
         qp.sv = sv;
@@ -288,11 +288,12 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
         qp.nblk = static_cast<int>(nblk);
         qp.codes = reinterpret_cast<uint8_t*>(wsb + code_off);
         qp.scales = reinterpret_cast<float*>(wsb + scale_off);
+        qp.widen = widen;
         return qp;
     };
-    const mha::QuantParams qq = quant(q, qv, nullptr, hq, sq, nq, off[0], off[3]);
-    const mha::QuantParams qk = quant(k, kv, k_mean, hk, sk, nk, off[1], off[4]);
-    const mha::QuantParams qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], off[5]);
+    const mha::QuantParams qq = quant(q, qv, nullptr, hq, sq, nq, off[0], off[3], false);
+    const mha::QuantParams qk = quant(k, kv, k_mean, hk, sk, nk, off[1], off[4], false);
+    const mha::QuantParams qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], off[5], true);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = mha::launch_quant_fp8(qq, qk, qvv, s);
     if (e != hipSuccess) return hip_status(e, "quant_fp8 launch");

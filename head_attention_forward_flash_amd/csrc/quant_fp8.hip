@@ -13,8 +13,10 @@
 //            for the last half-ulp above 448, which rounds to 448 anyway), then
 //            v_cvt_pk_fp8_f32 (round to nearest even)
 // Codes go to a token-padded [b, h, nblk*128, D] array (tokens past s are
-// written as zero codes), scales to [b, h, nblk].  HBM-bound: 2 bytes read and
-// 1 byte written per element.
+// written as zero codes), scales to [b, h, nblk].  For V the codes' values are
+// stored widened to bf16 instead (E4M3 values are exactly representable), which
+// is the form the P.V MFMA consumes.  HBM-bound: 2 bytes read and 1 byte (V: 2)
+// written per element.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -75,7 +77,7 @@ __device__ __forceinline__ void quant_block(const QuantParams& p, int bh_blk, fl
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
 
-    uint8_t* codes = p.codes + (static_cast<int64_t>(bh) * p.nblk * TOK + blk * TOK) * D;
+    const int64_t elem0 = static_cast<int64_t>(bh) * p.nblk * TOK + blk * TOK;   // first row of the block
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
         uint32_t packed[2];
@@ -89,7 +91,21 @@ __device__ __forceinline__ void quant_block(const QuantParams& p, int bh_blk, fl
             packed[half] = static_cast<uint32_t>(wv);
         }
         const int row = ps * ROWS + r0;
-        *reinterpret_cast<u32x2*>(codes + row * D + c0) = u32x2{packed[0], packed[1]};
+        if (p.widen) {
+            // the codes' values, widened to bf16 (every E4M3 value is a bf16 value)
+            uint32_t wide[4];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed[half]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed[half]), true);
+                wide[2 * half] = pack_bf16x2(lo[0], lo[1]);
+                wide[2 * half + 1] = pack_bf16x2(hi[0], hi[1]);
+            }
+            uint8_t* dst = p.codes + ((elem0 + row) * D + c0) * 2;
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wide[0], wide[1], wide[2], wide[3]};
+        } else {
+            *reinterpret_cast<u32x2*>(p.codes + (elem0 + row) * D + c0) = u32x2{packed[0], packed[1]};
+        }
     }
     if (tid == 0) p.scales[static_cast<int64_t>(bh) * p.nblk + blk] = scale;
 }

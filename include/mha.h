@@ -154,7 +154,7 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride,
  * ceil(sk/128); every region starts 256-byte aligned):
  *   q codes   uint8 [b, hq, nblk_q*128, d]     (token-padded, zero-filled tail)
  *   k codes   uint8 [b, hk, nblk_k*128, d]
- *   v codes   uint8 [b, hk, nblk_k*128, d]
+ *   v values  bf16  [b, hk, nblk_k*128, d]  (the E4M3 codes' values, widened exactly)
  *   q scales  fp32  [b, hq, nblk_q]
  *   k scales  fp32  [b, hk, nblk_k]
  *   v scales  fp32  [b, hk, nblk_k]
@@ -164,7 +164,7 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride,
 size_t mha_fwd_fp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d);
 
 /* Byte offsets of the six workspace regions above, in the order listed
- * (q codes, k codes, v codes, q scales, k scales, v scales); returns
+ * (q codes, k codes, v values, q scales, k scales, v scales); returns
  * MHA_ERR_SHAPE for invalid sizes. `offsets` is a host array of 6. */
 mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets);
 

@@ -28,11 +28,17 @@ def _fp8_call(q, k, v, mu, causal):
         raw = wsc[off[i]: off[i] + b * heads * n * 128 * d].reshape(b, heads, n * 128, d)
         return raw[:, :, :s, :].transpose(0, 2, 1, 3)          # -> [b, s, h, d]
 
+    def widened(i, heads, n, s):
+        # V is stored as its E4M3 values widened to bf16: return the codes those values encode
+        raw = ws[off[i]: off[i] + b * heads * n * 128 * d * 2].view(torch.bfloat16).float().cpu().numpy()
+        vals = raw.reshape(b, heads, n * 128, d)[:, :, :s, :].transpose(0, 2, 1, 3)
+        return oracle.e4m3_encode(vals.astype(np.float64))
+
     def scales(i, heads, n):
         return wsc[off[i]: off[i] + b * heads * n * 4].view(np.float32).reshape(b, heads, n)
 
     quant = {"q": (codes(0, hq, nq, sq), scales(3, hq, nq)), "k": (codes(1, hk, nk, sk), scales(4, hk, nk)),
-             "v": (codes(2, hk, nk, sk), scales(5, hk, nk))}
+             "v": (widened(2, hk, nk, sk), scales(5, hk, nk))}
     pad = {"q": wsc[off[0]: off[0] + b * hq * nq * 128 * d].reshape(b, hq, nq * 128, d)[:, :, sq:],
            "k": wsc[off[1]: off[1] + b * hk * nk * 128 * d].reshape(b, hk, nk * 128, d)[:, :, sk:]}
     return o.cpu(), lse.cpu(), quant, pad

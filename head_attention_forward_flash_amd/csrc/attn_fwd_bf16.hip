@@ -5,38 +5,44 @@
 // pathology" (Motivation; Technical Details: head-dim buckets 64, 128 and the
 // dqk=192/dv=128 "pe" bucket; Profile 2: pipelining depth as the main lever).
 //
-// Work decomposition: one workgroup of 4 waves per (batch, query head, block of
-// 128 query rows); each wave owns 32 query rows.  The kernel computes the
-// TRANSPOSED scores S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that every lane
-// holds one query row (lane % 32) and 32 of its keys per 64-key tile: the row
-// max and row sum then stay in the lane except for one exchange with lane ^ 32,
-// and the probabilities P^T are already laid out as the B operand of
-// O^T = V^T P^T (the key order inside one 16-key MFMA step is permuted the same
-// way on both operands, which leaves the contraction unchanged).
+// Work decomposition: one workgroup per (batch, query head, block of BM query
+// rows), one wave per 32 rows.  The kernel computes the TRANSPOSED scores
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds one query row
+// (lane % 32) and half of the keys of each 32-key block: the row max and row sum
+// stay in the lane except for one exchange with lane ^ 32, and the probabilities
+// P^T are already laid out as the B operand of O^T = V^T P^T (the key order
+// inside one 16-key MFMA step is permuted the same way on both operands, which
+// leaves the contraction unchanged).
 //
 //   Q      32 rows x d_qk per wave, loaded once into registers (B operand).
-//   K      64 x d_qk tile in LDS, row-major, rows padded by 16 bytes (A operand,
-//          one ds_read_b128 per MFMA, conflict-free across 8 consecutive rows).
-//   V      64 x d_v tile written TRANSPOSED into LDS (channel-major, keys
-//          contiguous) so the A operand of O^T = V^T P^T is two ds_read_b64.
-//   tiles  global -> registers for tile t+1 is issued before computing tile t
-//          (register double buffering); LDS holds one tile.  Each tile's loads
-//          use a buffer resource based at the tile, so their offsets are
-//          loop-invariant and the hardware zero-fills keys past sk.
+//   K, V   BN-key tiles stream global -> LDS by DMA (buffer_load ... lds) into two
+//          rings of two slots each, rows unpadded and 16-byte chunks XOR-swizzled
+//          for conflict-free reads: K rows feed the A operand of S^T with one
+//          ds_read_b128 per MFMA, V rows feed the A operand of O^T through
+//          transposing reads (ds_read_b64_tr_b16).
+//   loop   software-pipelined across tiles: while the exponentials of tile t
+//          run on the VALU, the MFMAs of S for tile t+1 already run, and the
+//          lane max of S_{t+1} is taken under the P.V MFMAs of tile t.  The
+//          instruction interleaving is fixed with scheduling group barriers, and
+//          the DMA of later tiles is spread over the MFMA stream so no wave stalls
+//          on a full address queue.
 //   causal key tiles past the block's last row are never loaded; masking is
-//          applied only on tiles that cross the diagonal or the ragged end.
+//          applied only on tiles that cross the diagonal or the ragged end, by
+//          setting the score to -inf, which the exponential maps to exactly 0.
 //   softmax online, in base 2: p = exp2(s*c - m*c) with c = |scale| * log2 e
-//          folded into one FMA (a negative scale negates Q, which is exact);
-//          the running max is only moved when a row's max grows by more than
-//          a factor 2^8 in probability, which keeps O and l consistent and
-//          rescales rarely; the row sum adds the bf16-rounded probabilities
-//          that enter P.V (v_dot2_f32_bf16), so O is normalised by exactly
-//          the weights it was built from.
+//          (at least FLT_MIN, so that a zero scale still maps -inf to 0) folded
+//          into one FMA (a negative scale negates Q, which is exact); the running
+//          max only moves when a row's max grows by more than a factor 2^8 in
+//          probability, which keeps O and l consistent and rescales rarely; the
+//          row sum adds the bf16-rounded probabilities that enter P.V
+//          (v_dot2_f32_bf16), so O is normalised by exactly the weights it was
+//          built from.
 //
 // Every global load goes through a buffer resource clamped to the (batch, head)
 // slice, so rows past sq / sk read as zero instead of faulting.
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -44,17 +50,42 @@
 namespace mha {
 namespace {
 
-constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr float kRescaleThreshold = 8.0f;      // log2 units
+constexpr float kMinScale = 1.17549435e-38f;   // FLT_MIN
 
-// Tile shape per head-dim pair: BM query rows per workgroup (32 per wave), BN keys per tile,
-// NSTAGE tiles in the LDS ring (NSTAGE - 1 in flight while one is computed).  128-row
-// workgroups run two per CU (80 KiB of LDS each); the 256-row one runs alone with 8 waves.
-// Chosen by A/B timing on MI355X: 256 rows halve the K/V traffic per FLOP, which pays off
-// for the wide d192/d128 tiles; three stages help only the short d64 tiles.
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kGrpValu = 0x002, kGrpMfma = 0x008, kGrpVmem = 0x010, kGrpDsRead = 0x100;
+
+// One slot of an interleaved region: one MFMA, then (while slots last) one VMEM
+// instruction, DS_PER LDS reads and VALU_PER vector ALU instructions.
+template <int I, int VMEM, int DS_SLOTS, int DS_PER, int VALU_SLOTS, int VALU_PER>
+__device__ __forceinline__ void sched_slot() {
+    __builtin_amdgcn_sched_group_barrier(kGrpMfma, 1, 0);
+    if constexpr (I < VMEM) __builtin_amdgcn_sched_group_barrier(kGrpVmem, 1, 0);
+    if constexpr (I < DS_SLOTS) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PER, 0);
+    if constexpr (I < VALU_SLOTS) __builtin_amdgcn_sched_group_barrier(kGrpValu, VALU_PER, 0);
+}
+
+// Scheduling pattern of a region with MFMAS matrix instructions fed by DS reads: DS_PRE
+// reads go first (the operands of the first MFMAs), the other DS_TOTAL - DS_PRE follow
+// DS_PER per MFMA, VMEM instructions go one per MFMA, and VALU instructions are spread
+// evenly over the MFMAs.
+template <int MFMAS, int DS_TOTAL, int DS_PRE, int DS_PER, int VALU, int VMEM, int... I>
+__device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
+    constexpr int DS_SLOTS = (DS_TOTAL - DS_PRE) / DS_PER;
+    constexpr int VALU_PER = (VALU + MFMAS - 1) / MFMAS;
+    constexpr int VALU_SLOTS = (VALU + VALU_PER - 1) / VALU_PER;
+    if constexpr (DS_PRE > 0) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PRE, 0);
+    (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
+}
+
+// Tile shape per head-dim pair: BM query rows per workgroup (32 per wave), BN keys per tile.
+// 128-row workgroups run two per CU; the 256-row one runs alone with 8 waves, which halves
+// the K/V traffic per FLOP of the wide d192/d128 tiles.
 template <int DQK, int DV> struct TileCfg;
-template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, NSTAGE = 3; };
-template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, NSTAGE = 2; };
-template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, NSTAGE = 2; };
+template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
+template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
+template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
@@ -62,39 +93,36 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
     constexpr int NWAVES = NTHREADS / 64;
     constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
-    constexpr int NSTAGE = TileCfg<DQK, DV>::NSTAGE;
-    constexpr int KB = BN / 32;                        // 32-key blocks per tile
     constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
     constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
     constexpr int KTILE = BN * KROWB;
     constexpr int VTILE = BN * VROWB;
-    constexpr int STAGE = KTILE + VTILE;      // one LDS stage: a K tile then a V tile
     constexpr int KDMA = KTILE / 1024 / NWAVES;   // 1 KiB DMA blocks per wave per K tile
     constexpr int VDMA = VTILE / 1024 / NWAVES;
     constexpr int KSTEPS = DQK / 16;          // MFMA k-steps for S^T
     constexpr int CBLK = DV / 32;             // 32-channel output blocks
+    static_assert(BN == 64, "the loop pipelines the two 32-key blocks of a tile");
     static_assert(KDMA * NWAVES * 1024 == KTILE && VDMA * NWAVES * 1024 == VTILE, "DMA blocks must cover the tiles");
+    static_assert(2 * (KTILE + VTILE) <= (BM == 128 ? 80 : 160) * 1024, "the workgroups of a CU must fit in LDS");
 
-    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring of 2 to 4 stages");
-    static_assert(NSTAGE * STAGE <= (BM == 128 ? 80 : 160) * 1024, "the workgroups of a CU must fit in LDS");
-    // The stages are distinct LDS objects: the compiler's wait insertion then knows that the
-    // DMA filling one stage cannot alias the fragment reads of another, and does not make the
-    // computation of tile t wait for the loads of later tiles.
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NSTAGE > 2 ? STAGE : 1024];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NSTAGE > 3 ? STAGE : 1024];
-    auto stage_ptr = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
-        constexpr int i = decltype(i_c)::value % NSTAGE;
-        if constexpr (i == 0) return lds0;
-        else if constexpr (i == 1) return lds1;
-        else if constexpr (i == 2) return lds2;
-        else return lds3;
+    // Two slots per ring, each a distinct LDS object: the compiler's wait insertion then
+    // knows that the DMA filling one slot cannot alias the fragment reads of another.
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VTILE];
+    auto k_slot = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        if constexpr (decltype(i_c)::value % 2 == 0) return k_lds0;
+        else return k_lds1;
+    };
+    auto v_slot = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        if constexpr (decltype(i_c)::value % 2 == 0) return v_lds0;
+        else return v_lds1;
     };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;     // query column of this lane in S^T / O^T
     const int half = lane >> 5;    // which half of the wave
 
@@ -131,16 +159,15 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
             qf[kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    const float c = fabsf(p.scale_log2);   // base-2 score scale, >= 0
+    const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
 
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // ---- K/V tiles go global -> LDS by DMA (buffer_load ... lds): lane l of a wave writes
-    //      16 bytes at block base + 16*l, and its global address decides what lands there.
-    //      Rows are unpadded and their 16-byte chunks XOR-swizzled so that the fragment reads
-    //      below are bank-conflict free on gfx950's LDS, which serves 256 bytes per clock
-    //      (16 lanes of a b128 read, 32 lanes of a b64 read):
+    // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
+    //      address decides what lands there.  The 16-byte chunks of a row are XOR-swizzled
+    //      so that the fragment reads are bank-conflict free on gfx950's LDS, which serves
+    //      256 bytes per clock (16 lanes of a b128 read, 32 lanes of a b64 read):
     //        K: the 16 rows one b128 read touches land on 16 distinct 16-byte bank groups;
     //        V: the 4 rows one transposing read touches land on 4 distinct 64-byte quarters.
     //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
@@ -170,25 +197,26 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
                                   ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
-    auto issue_tile = [&](int t, uint8_t* stage_base) __attribute__((always_inline)) {
-        const auto kr = tile_rsrc(kbase, p.kv, t);
-        const auto vr = tile_rsrc(vbase, p.vv, t);
-        uint8_t* kd = stage_base + wave * KDMA * 1024;
-        uint8_t* vd = stage_base + KTILE + wave * VDMA * 1024;
+    // past the last tile the buffer range is empty: nothing is read
+    auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+        const auto r = tile_rsrc(kbase, p.kv, t);
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i)
-            buffer_load_lds_b128(kr, kd + i * 1024, kgo[i]);
+        for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
+    };
+    auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+        const auto r = tile_rsrc(vbase, p.vv, t);
 #pragma unroll
-        for (int i = 0; i < VDMA; ++i)
-            buffer_load_lds_b128(vr, vd + i * 1024, vgo[i]);
+        for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
     };
 
     // LDS starts as zeros so that any row the DMA does not fill holds finite values
-    for (int i = tid; i < STAGE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(lds1)[i] = u32x4{0, 0, 0, 0};
-        if constexpr (NSTAGE > 2) reinterpret_cast<u32x4*>(lds2)[i] = u32x4{0, 0, 0, 0};
-        if constexpr (NSTAGE > 3) reinterpret_cast<u32x4*>(lds3)[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < KTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
+    }
+    for (int i = tid; i < VTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
 
@@ -198,7 +226,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
     float l_run = 0.f;       // this lane's partial row sum over its half of the keys
 
-    // fragment addresses inside a stage (bytes)
+    // fragment addresses inside a slot (bytes)
     const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
     const int t16 = lane & 15;
     // V transposing reads: lane t of a 16-lane group points at key (k0 + t/4), channel
@@ -206,63 +234,50 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     const int vkey_l = half * 4 + (t16 >> 2);                 // key offset inside a 16-key step
     const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3); // channel offset inside a 32-block
 
-    auto compute_tile = [&](int t, const uint8_t* kl) __attribute__((always_inline)) {
-        const uint8_t* vl = kl + KTILE;
+    // K fragment of k-step kk: row (kb*32 + col), 16-byte chunk (2*kk + half) ^ kx.  The swizzle
+    // only permutes chunks inside aligned groups of KSW chunks, so the address is one of
+    // KSW/2 per-lane offsets plus an immediate.
+    constexpr int KSW = KROWB % 256 == 0 ? 16 : 8;
+    uint32_t koff[KSW / 2];
+#pragma unroll
+    for (int j = 0; j < KSW / 2; ++j) koff[j] = col * KROWB + ((2 * j + half) ^ kx) * 16;
 
-        // ---- S^T = K Q^T: KB independent 32-key accumulators; K fragments are read KAHEAD
-        //      k-steps ahead of the MFMAs that use them
-        f32x16 s[KB];
+    // ---- S^T = K Q^T for the 32-key block kb of a K tile (one accumulator)
+    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
+        s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-        {
-            constexpr int KAHEAD = 3;
-            auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
-                const int chunk = (kk * 2 + half) ^ kx;
-                return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + (kb * 32 + col) * KROWB + chunk * 16));
-            };
-            bf16x8 fr[KSTEPS][KB];
-#pragma unroll
-            for (int kk = 0; kk < KAHEAD && kk < KSTEPS; ++kk)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) fr[kk][kb] = kfrag(kb, kk);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                if (kk + KAHEAD < KSTEPS) {
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) fr[kk + KAHEAD][kb] = kfrag(kb, kk + KAHEAD);
-                }
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk][kb], qf[kk], s[kb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const uint8_t* a_ptr = kl + koff[kk % (KSW / 2)] + (kk / (KSW / 2)) * KSW * 16 + kb * 32 * KROWB;
+            const auto a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_ptr));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
         }
-
-        // ---- mask (tiles crossing the diagonal or the ragged end only), tile max of raw scores
-        const int key0 = t * BN;
-        const bool need_mask = (key0 + BN > p.sk) || (CAUSAL && key0 + BN - 1 > wave_row0);
-        if (need_mask) {
+    };
+    // ---- scores of keys past sk, or above the diagonal, become -inf (block u = keys 32u ..)
+    auto need_mask = [&](int u) __attribute__((always_inline)) {
+        const int key0 = u * 32;
+        return (key0 + 32 > p.sk) || (CAUSAL && key0 + 31 > wave_row0);
+    };
+    auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = key0 + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                    if (key >= p.sk || (CAUSAL && key > my_row)) s[kb][j] = kNegInf;
-                }
-            }
+        for (int j = 0; j < 16; ++j) {
+            const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+            if (key >= p.sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
         }
-        float mt = __builtin_fmaxf(s[0][0], s[0][1]);
+    };
+    // ---- this lane's max over its 16 scores of a block
+    auto lane_max = [&](const f32x16& s) __attribute__((always_inline)) {
+        float a = __builtin_fmaxf(s[0], s[1]);
+        float b = __builtin_fmaxf(s[14], s[15]);
 #pragma unroll
-        for (int j = 2; j < 16; j += 2) mt = max3(mt, s[0][j], s[0][j + 1]);
+        for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
 #pragma unroll
-        for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; j += 2) mt = max3(mt, s[kb][j], s[kb][j + 1]);
-        mt = fmaxf(mt, swap_halves(mt));
-
-        // ---- online softmax with lazy rescaling (the reference max only moves when a row's
-        //      max grows by more than 2^8 in probability)
+        for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
+        return __builtin_fmaxf(a, b);
+    };
+    // ---- online softmax update from a block max (the reference max only moves when a row's
+    //      max grows by more than 2^8 in probability); returns m * c for the exponentials
+    auto softmax_update = [&](float mx) __attribute__((always_inline)) {
+        const float mt = fmaxf(mx, swap_halves(mx));
         const float m_new = fmaxf(m_run, mt);
         const bool grow = m_new > m_run && (m_run == kNegInf || (m_new - m_run) * c > kRescaleThreshold);
         if (__any(grow)) {
@@ -272,92 +287,162 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
             for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
             m_run = m_new;
         }
-        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-
-        constexpr int PSTEPS = BN / 16;   // 16-key MFMA steps of P.V
-        bf16x8 pf[PSTEPS];
+        return m_run == kNegInf ? 0.f : m_run * c;
+    };
+    // ---- P^T = exp2(S^T c - m c) rounded to bf16, as the B operands of two 16-key P.V steps
+    auto exp_block = [&](const f32x16& s, float mc, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < PSTEPS; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float s0 = s[ks >> 1][(ks & 1) * 8 + 2 * i];
-                const float s1 = s[ks >> 1][(ks & 1) * 8 + 2 * i + 1];
-                float p0 = fast_exp2(fmaf(s0, c, -mc));
-                float p1 = fast_exp2(fmaf(s1, c, -mc));
-                if (need_mask) {   // masked keys give exactly 0 whatever c is
-                    p0 = s0 == kNegInf ? 0.f : p0;
-                    p1 = s1 == kNegInf ? 0.f : p1;
-                }
+                const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, -mc));
+                const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, -mc));
                 w[i] = pack_bf16x2(p0, p1);
-                l_run = add_bf16_pair(w[i], l_run);   // the row sum of the rounded P fed to P.V
             }
             pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
-
-        // ---- O^T += V^T P^T: the A operand (32 channels x 16 keys) comes from two transposing
-        //      reads of row-major V; keys ks*16 + {half*4 .. +3} and {8 + half*4 .. +3} match
-        //      the key order of P^T's B operand.  Fragments of step ks+1 are read during step ks.
-        {
-            auto vfrag = [&](int cb, int ks) __attribute__((always_inline)) {
+    };
+    // ---- row sum of the rounded P fed to P.V
+    auto row_sum = [&](const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        float a = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+        }
+        l_run += a;
+    };
+    // ---- O^T += V^T P^T over the 32-key block kb of a V tile: the A operand (32 channels x
+    //      16 keys) comes from two transposing reads of row-major V; keys ks*16 +
+    //      {half*4 .. +3} and {8 + half*4 .. +3} match the key order of P^T's B operand
+    auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) {
                 u32x2 part[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int key = ks * 16 + r * 8 + vkey_l;
+                    const int key = kb * 32 + ks * 16 + r * 8 + vkey_l;
                     const int ch = cb * 32 + vch_l;
                     const int chunk = (ch >> 3) ^ vswz(key);
-                    const uint8_t* a = vl + key * VROWB + chunk * 16 + (ch & 7) * 2;
-                    part[r] = lds_read_tr16_b64(a);
+                    part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
                 }
-                return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
-            };
-            bf16x8 a[2][CBLK];
-#pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) a[0][cb] = vfrag(cb, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < PSTEPS; ++ks) {
-                if (ks + 1 < PSTEPS) {
-#pragma unroll
-                    for (int cb = 0; cb < CBLK; ++cb) a[(ks + 1) & 1][cb] = vfrag(cb, ks + 1);
-                }
-#pragma unroll
-                for (int cb = 0; cb < CBLK; ++cb)
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][cb], pf[ks], oacc[cb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
             }
         }
     };
 
-    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed.  The
-    //      barrier makes every wave's part of tile t visible and guarantees that every wave
-    //      finished tile t - 1, whose stage the next DMA overwrites.
-    constexpr int DMA_PER_TILE = KDMA + VDMA;
-    constexpr int VM_LEFT = (NSTAGE - 2) * DMA_PER_TILE;   // DMAs of younger tiles still in flight
-    static_assert(VM_LEFT < 64, "vmcnt is 6 bits");
-    constexpr int WAIT_TILE = (VM_LEFT & 15) | ((VM_LEFT >> 4) << 14) | 0x0F70;   // vmcnt(VM_LEFT)
-    auto prologue = [&](auto i_c) __attribute__((always_inline)) {
-        if constexpr (decltype(i_c)::value < NSTAGE - 1) issue_tile(decltype(i_c)::value, stage_ptr(i_c));
+    // Instruction counts of the interleaved regions (per wave and 32-key block).
+    constexpr int EXP_VALU = 16 + 16 + 8;           // FMA + exp per score, one pack per pair
+    constexpr int PV_MFMA = 2 * CBLK;               // two transposing V reads per MFMA
+    constexpr int PV_VALU = 8 + 8 + 1;              // row-sum dot2 + next block's max chain
+    constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
+    constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
+    constexpr int WAIT_K0 = (VM_PROLOGUE & 15) | ((VM_PROLOGUE >> 4) << 14) | 0x0F70;
+    static_assert(VM_PROLOGUE < 64, "vmcnt is 6 bits");
+    // region A: S of the next block (KSTEPS MFMAs, one K read each) under the exponentials
+    //           of the current block
+    auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float mc,
+                        bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        qk_block(kl, kb, sn);
+        exp_block(s, mc, pf);
+        // keep the exponentials here: without a use inside the region the compiler would sink
+        // them to the P.V MFMAs that consume them
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+        sched_region<KSTEPS, KSTEPS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
+        __builtin_amdgcn_sched_barrier(0);
     };
-    prologue(std::integral_constant<int, 0>{});
-    prologue(std::integral_constant<int, 1>{});
-    prologue(std::integral_constant<int, 2>{});
-    for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
-        auto step = [&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = decltype(j_c)::value;
-            const int t = t0 + j;
-            if (j < NSTAGE && t < ntiles) {
-                __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // this wave's part of tile t has landed
-                __syncthreads();
-                // past the last tile: empty buffer range, nothing is read
-                issue_tile(t + NSTAGE - 1, stage_ptr(std::integral_constant<int, j + NSTAGE - 1>{}));
-                compute_tile(t, stage_ptr(j_c));
-            }
-        };
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        if constexpr (NSTAGE > 2) step(std::integral_constant<int, 2>{});
-        if constexpr (NSTAGE > 3) step(std::integral_constant<int, 3>{});
+    // region B: P.V of the current block under its row sum and the next block's lane max
+    auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], const f32x16& sn,
+                        auto vmem_c) __attribute__((always_inline)) {
+        pv_block(vl, kb, pf);
+        row_sum(pf);
+        const float mx = lane_max(sn);
+        sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+            std::make_integer_sequence<int, PV_MFMA>{});
+        __builtin_amdgcn_sched_barrier(0);
+        return mx;
+    };
+
+    // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks: block
+    //      u's exponentials run under the S MFMAs of block u+1, and block u's P.V under the
+    //      lane max of block u+1.  Tile t's K sits in k slot t%2 and its V in v slot t%2.
+    //      The barrier of iteration t (after the S MFMAs of its second block) guarantees
+    //      that every wave's part of V_t and K_{t+1} has landed and that no wave still reads
+    //      K_t or V_{t-1}: their slots then take K_{t+2} and V_{t+1}.
+    using NoVmem = std::integral_constant<int, 0>;
+    using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
+    // a tile that is not the last: its two blocks and the S of the next tile's first block
+    auto iteration = [&](int t, auto par_c, f32x16& s, float& mx) __attribute__((always_inline)) {
+        using Cur = std::integral_constant<int, decltype(par_c)::value>;
+        using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+        f32x16 sn;
+        bf16x8 pf[2];
+        // block 2t (exponentials, P.V) with block 2t+1 (S, max)
+        float mc = softmax_update(mx);
+        region_a(k_slot(Cur{}), 1, sn, s, mc, pf);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(t + 2, k_slot(Cur{}));
+        issue_v(t + 1, v_slot(Nxt{}));
+        mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{});
+        s = sn;
+        // block 2t+1 with block 2t+2 (the first block of the next tile)
+        mc = softmax_update(mx);
+        region_a(k_slot(Nxt{}), 0, sn, s, mc, pf);
+        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
+        __builtin_amdgcn_sched_barrier(0);
+        mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{});
+        s = sn;
+    };
+    // the last tile: its two blocks, nothing further to load
+    auto last = [&](int t, auto par_c, const f32x16& s0, float mx) __attribute__((always_inline)) {
+        using Cur = std::integral_constant<int, decltype(par_c)::value>;
+        f32x16 sn;
+        bf16x8 pf[2];
+        float mc = softmax_update(mx);
+        region_a(k_slot(Cur{}), 1, sn, s0, mc, pf);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{});
+        mc = softmax_update(mx);
+        exp_block(sn, mc, pf);
+        row_sum(pf);
+        pv_block(v_slot(Cur{}), 1, pf);
+    };
+
+    if (ntiles > 0) {
+        using Zero = std::integral_constant<int, 0>;
+        using One = std::integral_constant<int, 1>;
+        issue_k(0, k_slot(Zero{}));
+        issue_v(0, v_slot(Zero{}));
+        issue_k(1, k_slot(One{}));
+        __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
+        __syncthreads();
+        f32x16 s;
+        qk_block(k_slot(Zero{}), 0, s);
+        if (need_mask(0)) mask_block(0, s);
+        float mx = lane_max(s);
+        int t = 0;
+        for (; t + 2 < ntiles; t += 2) {
+            iteration(t, Zero{}, s, mx);
+            iteration(t + 1, One{}, s, mx);
+        }
+        if (t + 1 < ntiles) {
+            iteration(t, Zero{}, s, mx);
+            last(t + 1, One{}, s, mx);
+        } else {
+            last(t, Zero{}, s, mx);
+        }
     }
 
     // ---- epilogue: normalise, store O (bf16) and LSE

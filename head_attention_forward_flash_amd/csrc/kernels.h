@@ -64,7 +64,7 @@ hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const Qu
 struct Fp8AttnParams {
     const uint8_t* q;   // [b, hq, nq*128, d] codes
     const uint8_t* k;   // [b, hk, nk*128, d]
-    const uint8_t* v;   // [b, hk, nk*128, d]
+    const uint8_t* v;   // [b, hk, nk*128, d] bf16: the E4M3 codes' values, widened exactly
     const float* q_scale;  // [b, hq, nq]
     const float* k_scale;  // [b, hk, nk]
     const float* v_scale;  // [b, hk, nk]

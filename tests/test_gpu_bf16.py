@@ -168,3 +168,21 @@ def test_large_score_magnitudes():
     v = workloads.make_random((1, 256, 2, 64), 63)
     _check_all(q, k, v, False, "large scores", scale=0.5)
     _check_all(q, k, v, True, "large scores causal", scale=0.5)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+def test_negative_and_zero_scale(dims):
+    # A negative scale flips the score order (the kernel negates Q, which is exact); a zero
+    # scale makes every unmasked key equally likely, so O is the running mean of V and the
+    # LSE is log(number of unmasked keys).  Both against the oracle, causal and not.
+    dqk, dv = dims
+    seed = 3000 + dqk
+    q = workloads.make_random((1, 150, 2, dqk), seed)
+    k = workloads.make_random((1, 150, 2, dqk), seed + 1)
+    v = workloads.make_random((1, 150, 2, dv), seed + 2)
+    for causal in (False, True):
+        _check_all(q, k, v, causal, f"d{dqk} scale=-0.3 causal={causal}", scale=-0.3)
+        _check_all(q, k, v, causal, f"d{dqk} scale=0 causal={causal}", scale=0.0)
+    o, lse = _run(q, k, v, True, 0.0)
+    counts = np.arange(1, 151, dtype=np.float64)
+    np.testing.assert_allclose(lse[0, 0].numpy(), np.log(counts), atol=2 ** -8)

@@ -6,23 +6,28 @@
 // quant_fp8: E4M3 codes of Q and K - mean, the E4M3 values of V widened exactly
 // to bf16, and one fp32 scale per (batch, head, 128-token block) for each.
 //
-// Same pipeline as the bf16 kernel (4 waves x 32 query rows, 64-key tiles, one
-// query per lane in S^T, K/V tiles staged into a ring of LDS stages by DMA):
-//   S^T = K8 Q8^T  on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate),
-//                  two k-steps of 64 channels; both operands read 32 bytes of
-//                  their row per lane, so the MFMA's channel order cancels out;
+// Same organisation as the bf16 kernel (4 waves x 32 query rows, 64-key tiles,
+// one query per lane in S^T, K and V tiles streamed by DMA into two-slot LDS
+// rings, the loop software-pipelined over 32-key blocks):
+//   S^T = K8 Q8^T  on v_mfma_scale_f32_32x32x64_f8f6f4 with zero scales (plain
+//                  E4M3 x E4M3, fp32 accumulate), two k-steps of 64 channels;
+//                  both operands read 32 bytes of their row per lane, so the
+//                  MFMA's channel order cancels out;
 //   scores         t = s * (scale_q * scale_k * |softmax_scale| * log2 e): one
 //                  factor per tile, since a 64-key tile sits inside one
 //                  128-token scale block and the 128 query rows are one block;
-//                  the factor and the running max fold into one FMA before exp2;
+//                  the running max is kept in these scaled base-2 units;
 //   P.V            on bf16 MFMA; the V operand comes from transposing LDS reads of
 //                  the widened V values, and the V block scale enters P through
 //                  the exponent (p' = exp2(t - m + log2 scale_v)) before P is
 //                  rounded to bf16;
 //   l              sums the bf16 P' fed to P.V (v_dot2_f32_bf16), divided by the
-//                  tile's V scale once per tile.
+//                  V scale of its block.
+// Masked scores are -inf; the per-tile factor is at least FLT_MIN, so they reach
+// the exponential as -inf and come out as exactly 0.
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -34,37 +39,62 @@ constexpr int BM = 128;          // query rows per workgroup = one Q scale block
 constexpr int BN = 64;           // keys per tile (half a K/V scale block)
 constexpr int D = 128;
 constexpr int NTHREADS = 256;
-constexpr int NSTAGE = 3;
-constexpr float kRescaleThreshold = 8.0f;
+constexpr float kRescaleThreshold = 8.0f;     // log2 units
+constexpr float kMinFactor = 1.17549435e-38f;   // FLT_MIN
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kGrpValu = 0x002, kGrpMfma = 0x008, kGrpVmem = 0x010, kGrpDsRead = 0x100;
+
+template <int I, int VMEM, int DS_SLOTS, int DS_PER, int VALU_SLOTS, int VALU_PER>
+__device__ __forceinline__ void sched_slot() {
+    __builtin_amdgcn_sched_group_barrier(kGrpMfma, 1, 0);
+    if constexpr (I < VMEM) __builtin_amdgcn_sched_group_barrier(kGrpVmem, 1, 0);
+    if constexpr (I < DS_SLOTS) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PER, 0);
+    if constexpr (I < VALU_SLOTS) __builtin_amdgcn_sched_group_barrier(kGrpValu, VALU_PER, 0);
+}
+
+// MFMAS matrix instructions, DS_PRE reads first, the other DS reads DS_PER per MFMA, VMEM
+// instructions one per MFMA, VALU instructions spread evenly.
+template <int MFMAS, int DS_TOTAL, int DS_PRE, int DS_PER, int VALU, int VMEM, int... I>
+__device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
+    constexpr int DS_SLOTS = (DS_TOTAL - DS_PRE) / DS_PER;
+    constexpr int VALU_PER = (VALU + MFMAS - 1) / MFMAS;
+    constexpr int VALU_SLOTS = (VALU + VALU_PER - 1) / VALU_PER;
+    if constexpr (DS_PRE > 0) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PRE, 0);
+    (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
+}
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
+    constexpr int NWAVES = NTHREADS / 64;
     constexpr int KROWB = D;                  // bytes per K8 row
     constexpr int VROWB = D * 2;              // bytes per widened V row
     constexpr int KTILE = BN * KROWB;
     constexpr int VTILE = BN * VROWB;
-    constexpr int STAGE = KTILE + VTILE;
-    constexpr int KDMA = KTILE / 1024 / 4;    // 1 KiB DMA blocks per wave per tile
-    constexpr int VDMA = VTILE / 1024 / 4;
+    constexpr int KDMA = KTILE / 1024 / NWAVES;   // 1 KiB DMA blocks per wave per tile
+    constexpr int VDMA = VTILE / 1024 / NWAVES;
     constexpr int CBLK = D / 32;
-    static_assert(KDMA * 4 * 1024 == KTILE && VDMA * 4 * 1024 == VTILE, "DMA blocks must cover the tiles");
-    static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per CU must fit in LDS");
+    static_assert(KDMA * NWAVES * 1024 == KTILE && VDMA * NWAVES * 1024 == VTILE, "DMA blocks must cover the tiles");
+    static_assert(2 * (KTILE + VTILE) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
-    // distinct LDS objects per stage (see the bf16 kernel: keeps the DMA of later tiles from
-    // gating the fragment reads of the current one)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGE];
-    auto stage_ptr = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
-        constexpr int i = decltype(i_c)::value % NSTAGE;
-        if constexpr (i == 0) return lds0;
-        else if constexpr (i == 1) return lds1;
-        else return lds2;
+    // each ring slot is its own LDS object, so a DMA into one slot never gates the fragment
+    // reads of another in the compiler's wait insertion
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VTILE];
+    auto k_slot = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        if constexpr (decltype(i_c)::value % 2 == 0) return k_lds0;
+        else return k_lds1;
+    };
+    auto v_slot = [&](auto i_c) __attribute__((always_inline)) -> uint8_t* {
+        if constexpr (decltype(i_c)::value % 2 == 0) return v_lds0;
+        else return v_lds1;
     };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
 
@@ -109,6 +139,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
+    // per-tile factors: the scores' base-2 factor (>= FLT_MIN) and the V block scale
+    struct TileScale {
+        float c, log2_sv, inv_sv;
+    };
+    auto tile_scale = [&](int t) __attribute__((always_inline)) {
+        const int kblk = min((t * BN) / BM, p.nk - 1);   // past the last tile: any valid block
+        const float sv = v_scale[kblk];
+        return TileScale{fmaxf(cq * k_scale[kblk], kMinFactor), __log2f(sv), 1.f / sv};
+    };
+
     // ---- DMA layout (see the bf16 kernel): K8 rows of 128 B keep chunk c of row r at
     //      c ^ ((r >> 1) & 7); widened V rows of 256 B keep chunk c of key r at c ^ 4*(r & 3).
     auto kswz = [](int r) __attribute__((always_inline)) { return (r >> 1) & 7; };
@@ -126,34 +166,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         const int r = pos / VROWB, pc = (pos % VROWB) / 16;
         vgo[i] = static_cast<uint32_t>(r * VROWB + (pc ^ vswz(r)) * 16);
     }
+    // (the descriptor's fields go through readfirstlane: a descriptor the compiler cannot prove
+    // uniform would wrap every DMA instruction in a loop over lanes)
     auto tile_rsrc = [&](const uint8_t* base, uint32_t slice, uint32_t rowb, int t) __attribute__((always_inline)) {
         const uint32_t start = static_cast<uint32_t>(t) * BN * rowb;
         const uint32_t left = start < slice ? slice - start : 0u;
-        return make_rsrc(left ? base + start : base, left);
+        const uint64_t addr = uniform_u64(reinterpret_cast<uint64_t>(base) + (left ? start : 0u));
+        return make_rsrc(reinterpret_cast<const void*>(addr), static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(left)));
     };
-    auto issue_tile = [&](int t, uint8_t* stage_base) __attribute__((always_inline)) {
-        // tiles past the padded key range read nothing (empty buffer range)
-        const auto kr = tile_rsrc(kbase, kslice, KROWB, t);
-        const auto vr = tile_rsrc(vbase, vslice, VROWB, t);
-        uint8_t* kd = stage_base + wave * KDMA * 1024;
-        uint8_t* vd = stage_base + KTILE + wave * VDMA * 1024;
+    // tiles past the padded key range read nothing (empty buffer range)
+    auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+        const auto r = tile_rsrc(kbase, kslice, KROWB, t);
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(kr, kd + i * 1024, kgo[i]);
+        for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
+    };
+    auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+        const auto r = tile_rsrc(vbase, vslice, VROWB, t);
 #pragma unroll
-        for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(vr, vd + i * 1024, vgo[i]);
+        for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
     };
 
-    for (int i = tid; i < STAGE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(lds1)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(lds2)[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < KTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
+    }
+    for (int i = tid; i < VTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
 
     f32x16 oacc[CBLK];
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
-    float m_run = kNegInf;   // running max in base-2 units of scaled scores
+    float m_run = kNegInf;   // running max in scaled base-2 units, same in lane and lane^32
     float l_run = 0.f;
 
     const int kx = kswz(col);
@@ -161,58 +207,46 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const int vkey_l = half * 4 + (t16 >> 2);
     const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3);
 
-    auto compute_tile = [&](int t, const uint8_t* kl) __attribute__((always_inline)) {
-        const uint8_t* vl = kl + KTILE;
-        const int kblk = (t * BN) / BM;
-        const float c = cq * k_scale[kblk];            // this tile's base-2 score factor
-        const float log2_sv = __log2f(v_scale[kblk]);  // V block scale, folded into P
-        const float inv_sv = 1.f / v_scale[kblk];
-
-        // ---- S^T = K8 Q8^T: two 32-key accumulators, two k-steps of 64 channels
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        {
-            i32x8 fr[2][2];
+    // ---- S^T = K8 Q8^T for the 32-key block kb of a K tile
+    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
+        const uint8_t* row = kl + (kb * 32 + col) * KROWB;
+        s = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint8_t* row = kl + (kb * 32 + col) * KROWB;
-                    const int c0 = (ks * 4 + half * 2) ^ kx, c1 = (ks * 4 + half * 2 + 1) ^ kx;
-                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + c0 * 16);
-                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + c1 * 16);
-                    fr[ks][kb] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                       (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[ks][kb], qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c0 = (ks * 4 + half * 2) ^ kx, c1 = (ks * 4 + half * 2 + 1) ^ kx;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + c0 * 16);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + c1 * 16);
+            const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s, 0, 0, 0, 0, 0, 0);
         }
-
-        const int key0 = t * BN;
-        const bool need_mask = (key0 + BN > p.sk) || (CAUSAL && key0 + BN - 1 > wave_row0);
-        if (need_mask) {
+    };
+    auto need_mask = [&](int u) __attribute__((always_inline)) {
+        const int key0 = u * 32;
+        return (key0 + 32 > p.sk) || (CAUSAL && key0 + 31 > wave_row0);
+    };
+    auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = key0 + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                    if (key >= p.sk || (CAUSAL && key > my_row)) s[kb][j] = kNegInf;
-                }
-            }
+        for (int j = 0; j < 16; ++j) {
+            const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+            if (key >= p.sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
         }
-        float mt = __builtin_fmaxf(s[0][0], s[0][1]);
+    };
+    // ---- the row's max over a block in scaled base-2 units (c > 0 keeps the order)
+    auto row_max = [&](const f32x16& s, float c) __attribute__((always_inline)) {
+        float a = __builtin_fmaxf(s[0], s[1]);
+        float b = __builtin_fmaxf(s[14], s[15]);
 #pragma unroll
-        for (int j = 2; j < 16; j += 2) mt = max3(mt, s[0][j], s[0][j + 1]);
+        for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) mt = max3(mt, s[1][j], s[1][j + 1]);
-        mt = fmaxf(mt, swap_halves(mt));
-        mt = mt == kNegInf ? kNegInf : mt * c;   // tile max in scaled base-2 units
-
+        for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
+        const float lm = __builtin_fmaxf(a, b);
+        const float mt = fmaxf(lm, swap_halves(lm));
+        return mt == kNegInf ? kNegInf : mt * c;
+    };
+    // ---- online softmax update (lazy: the reference max moves only when it grows by more
+    //      than 2^8 in probability); returns the exponent bias -m + log2 scale_v
+    auto softmax_update = [&](float mt, float log2_sv) __attribute__((always_inline)) {
         const float m_new = fmaxf(m_run, mt);
         const bool grow = m_new > m_run && (m_run == kNegInf || m_new - m_run > kRescaleThreshold);
         if (__any(grow)) {
@@ -222,82 +256,159 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
             for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
             m_run = m_new;
         }
-        // p' = p * scale_v = exp2(s*c - m + log2 scale_v): the V block scale rides in the exponent
-        const float bias = (m_run == kNegInf ? 0.f : -m_run) + log2_sv;
-
-        bf16x8 pf[4];
-        float l_tile = 0.f;
+        return (m_run == kNegInf ? 0.f : -m_run) + log2_sv;
+    };
+    // ---- P'^T = exp2(S^T c + bias) rounded to bf16, as the B operands of two 16-key steps
+    auto exp_block = [&](const f32x16& s, float c, float bias, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float s0 = s[ks >> 1][(ks & 1) * 8 + 2 * i];
-                const float s1 = s[ks >> 1][(ks & 1) * 8 + 2 * i + 1];
-                float p0 = fast_exp2(fmaf(s0, c, bias));
-                float p1 = fast_exp2(fmaf(s1, c, bias));
-                if (need_mask) {
-                    p0 = s0 == kNegInf ? 0.f : p0;
-                    p1 = s1 == kNegInf ? 0.f : p1;
-                }
+                const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, bias));
+                const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, bias));
                 w[i] = pack_bf16x2(p0, p1);
-                l_tile = add_bf16_pair(w[i], l_tile);
             }
             pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
-        l_run = fmaf(l_tile, inv_sv, l_run);   // back to unscaled probabilities
-
-        // ---- O^T += V^T P'^T from transposing reads of the widened V rows
-        {
-            auto vfrag = [&](int cb, int ks) __attribute__((always_inline)) {
+    };
+    // ---- row sum of the bf16 P' fed to P.V, back to unscaled probabilities
+    auto row_sum = [&](const bf16x8 (&pf)[2], float inv_sv) __attribute__((always_inline)) {
+        float a = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+        }
+        l_run = fmaf(a, inv_sv, l_run);
+    };
+    // ---- O^T += V^T P'^T over the 32-key block kb of a V tile (transposing reads)
+    auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) {
                 u32x2 part[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int key = ks * 16 + r * 8 + vkey_l;
+                    const int key = kb * 32 + ks * 16 + r * 8 + vkey_l;
                     const int ch = cb * 32 + vch_l;
                     const int chunk = (ch >> 3) ^ vswz(key);
                     part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
                 }
-                return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
-            };
-            bf16x8 a[2][CBLK];
-#pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) a[0][cb] = vfrag(cb, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks + 1 < 4) {
-#pragma unroll
-                    for (int cb = 0; cb < CBLK; ++cb) a[(ks + 1) & 1][cb] = vfrag(cb, ks + 1);
-                }
-#pragma unroll
-                for (int cb = 0; cb < CBLK; ++cb)
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][cb], pf[ks], oacc[cb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
             }
         }
     };
 
-    // ---- main loop: NSTAGE - 1 tiles stream into the ring while tile t is computed
-    constexpr int VM_LEFT = (NSTAGE - 2) * (KDMA + VDMA);
-    static_assert(VM_LEFT < 16, "vmcnt immediate");
-    constexpr int WAIT_TILE = VM_LEFT | 0x0F70;
-    issue_tile(0, lds0);
-    issue_tile(1, lds1);
-    for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
-        auto step = [&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = decltype(j_c)::value;
-            const int t = t0 + j;
-            if (t < ntiles) {
-                __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // this wave's part of tile t has landed
-                __syncthreads();
-                issue_tile(t + NSTAGE - 1, stage_ptr(std::integral_constant<int, j + NSTAGE - 1>{}));
-                compute_tile(t, stage_ptr(j_c));
-            }
-        };
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
+    constexpr int EXP_VALU = 16 + 16 + 8;
+    constexpr int PV_MFMA = 2 * CBLK;
+    constexpr int PV_VALU = 8 + 8 + 5;
+    constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
+    constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
+    static_assert(VM_PROLOGUE < 16, "vmcnt immediate");
+    constexpr int WAIT_K0 = VM_PROLOGUE | 0x0F70;
+    // region A: S of the next block (2 fp8 MFMAs, 4 K reads) under the exponentials of the
+    //           current block
+    auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float c, float bias,
+                        bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        qk_block(kl, kb, sn);
+        exp_block(s, c, bias, pf);
+        // keep the exponentials here: without a use inside the region the compiler would sink
+        // them to the P.V MFMAs that consume them
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+        sched_region<2, 4, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // region B: P.V of the current block under its row sum and the next block's row max
+    auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], float inv_sv, const f32x16& sn,
+                        float c_next, auto vmem_c) __attribute__((always_inline)) {
+        pv_block(vl, kb, pf);
+        row_sum(pf, inv_sv);
+        const float mt = row_max(sn, c_next);
+        sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+            std::make_integer_sequence<int, PV_MFMA>{});
+        __builtin_amdgcn_sched_barrier(0);
+        return mt;
+    };
+
+    // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks (as in the
+    //      bf16 kernel).  Tile t's K sits in k slot t%2 and its V in v slot t%2; the barrier
+    //      of iteration t guarantees that every wave's part of V_t and K_{t+1} has landed and
+    //      that no wave still reads K_t or V_{t-1}: their slots then take K_{t+2}, V_{t+1}.
+    using NoVmem = std::integral_constant<int, 0>;
+    using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
+    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc) __attribute__((always_inline)) {
+        using Cur = std::integral_constant<int, decltype(par_c)::value>;
+        using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+        const TileScale sc_next = tile_scale(t + 1);
+        f32x16 sn;
+        bf16x8 pf[2];
+        // block 2t (exponentials, P.V) with block 2t+1 (S, max)
+        float bias = softmax_update(mt, sc.log2_sv);
+        region_a(k_slot(Cur{}), 1, sn, s, sc.c, bias, pf);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(t + 2, k_slot(Cur{}));
+        issue_v(t + 1, v_slot(Nxt{}));
+        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{});
+        s = sn;
+        // block 2t+1 with block 2t+2 (the first block of the next tile)
+        bias = softmax_update(mt, sc.log2_sv);
+        region_a(k_slot(Nxt{}), 0, sn, s, sc.c, bias, pf);
+        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
+        __builtin_amdgcn_sched_barrier(0);
+        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, sn, sc_next.c, NoVmem{});
+        s = sn;
+        sc = sc_next;
+    };
+    // the last tile: its two blocks, nothing further to load
+    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc) __attribute__((always_inline)) {
+        using Cur = std::integral_constant<int, decltype(par_c)::value>;
+        f32x16 sn;
+        bf16x8 pf[2];
+        float bias = softmax_update(mt, sc.log2_sv);
+        region_a(k_slot(Cur{}), 1, sn, s0, sc.c, bias, pf);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, NoVmem{});
+        bias = softmax_update(mt, sc.log2_sv);
+        exp_block(sn, sc.c, bias, pf);
+        row_sum(pf, sc.inv_sv);
+        pv_block(v_slot(Cur{}), 1, pf);
+    };
+
+    if (ntiles > 0) {
+        using Zero = std::integral_constant<int, 0>;
+        using One = std::integral_constant<int, 1>;
+        issue_k(0, k_slot(Zero{}));
+        issue_v(0, v_slot(Zero{}));
+        issue_k(1, k_slot(One{}));
+        __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
+        __syncthreads();
+        TileScale sc = tile_scale(0);
+        f32x16 s;
+        qk_block(k_slot(Zero{}), 0, s);
+        if (need_mask(0)) mask_block(0, s);
+        float mt = row_max(s, sc.c);
+        int t = 0;
+        for (; t + 2 < ntiles; t += 2) {
+            iteration(t, Zero{}, s, mt, sc);
+            iteration(t + 1, One{}, s, mt, sc);
+        }
+        if (t + 1 < ntiles) {
+            iteration(t, Zero{}, s, mt, sc);
+            last(t + 1, One{}, s, mt, sc);
+        } else {
+            last(t, Zero{}, s, mt, sc);
+        }
     }
 
     const float l_tot = l_run + swap_halves(l_run);

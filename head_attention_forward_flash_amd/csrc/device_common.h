@@ -30,6 +30,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// A wave-uniform 64-bit value, moved through readfirstlane half by half so that the compiler
+// keeps it (and a buffer descriptor built from it) in scalar registers.  readfirstlane
+// returns a signed int: each half goes back through uint32_t before widening, or a set bit 31
+// of the low half would sign-extend into the high half.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 __device__ __forceinline__ u32x4 buffer_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }

@@ -49,24 +49,51 @@ __global__ __launch_bounds__(NT) void k_moments_kernel(const GateParams p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) s1[i] = s2[i] = 0.f;
 
-    for (int t = t_begin + rg; t < t_end; t += RG) {
-        const int64_t key = static_cast<int64_t>(t) * p.key_stride;
-        const uint32_t off = static_cast<uint32_t>((key * p.kv.ss + c0) * 2);
+    // The thread's rows t_begin + rg, + RG, ... are summed in that order.  All of a batch of
+    // ROWS_IN_FLIGHT rows is loaded before any is added (rows past t_end read as zeros
+    // through an out-of-range offset and are not added), so the loads overlap.
+    constexpr int ROWS_IN_FLIGHT = kGateChunk / RG;
+    for (int t0 = t_begin + rg; t0 < t_end; t0 += RG * ROWS_IN_FLIGHT) {
         if constexpr (VEC) {
-            const u32x4 w = buffer_load_b128(rs, off);
+            u32x4 w[ROWS_IN_FLIGHT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = bf16_bits_to_float(w[i] & 0xffffu);
-                const float hi = bf16_bits_to_float(w[i] >> 16);
-                s1[2 * i] += lo;
-                s2[2 * i] += lo * lo;
-                s1[2 * i + 1] += hi;
-                s2[2 * i + 1] += hi * hi;
+            for (int j = 0; j < ROWS_IN_FLIGHT; ++j) {
+                const int t = t0 + j * RG;
+                const int64_t key = static_cast<int64_t>(t) * p.key_stride;
+                const uint32_t off = t < t_end ? static_cast<uint32_t>((key * p.kv.ss + c0) * 2) : kOutOfRange;
+                w[j] = buffer_load_b128(rs, off);
+            }
+#pragma unroll
+            for (int j = 0; j < ROWS_IN_FLIGHT; ++j) {
+                if (t0 + j * RG < t_end) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = bf16_bits_to_float(w[j][i] & 0xffffu);
+                        const float hi = bf16_bits_to_float(w[j][i] >> 16);
+                        s1[2 * i] += lo;
+                        s2[2 * i] += lo * lo;
+                        s1[2 * i + 1] += hi;
+                        s2[2 * i + 1] += hi * hi;
+                    }
+                }
             }
         } else {
-            const float x = bf16_bits_to_float(buffer_load_b16(rs, off));
-            s1[0] += x;
-            s2[0] += x * x;
+            uint16_t w[ROWS_IN_FLIGHT];
+#pragma unroll
+            for (int j = 0; j < ROWS_IN_FLIGHT; ++j) {
+                const int t = t0 + j * RG;
+                const int64_t key = static_cast<int64_t>(t) * p.key_stride;
+                const uint32_t off = t < t_end ? static_cast<uint32_t>((key * p.kv.ss + c0) * 2) : kOutOfRange;
+                w[j] = buffer_load_b16(rs, off);
+            }
+#pragma unroll
+            for (int j = 0; j < ROWS_IN_FLIGHT; ++j) {
+                if (t0 + j * RG < t_end) {
+                    const float x = bf16_bits_to_float(w[j]);
+                    s1[0] += x;
+                    s2[0] += x * x;
+                }
+            }
         }
     }
 #pragma unroll
@@ -97,9 +124,23 @@ __global__ __launch_bounds__(NT) void k_fold_gate_kernel(const GateParams p) {
     if (tid < D && p.n_samples > 0) {
         const float* src = p.partial + static_cast<int64_t>(bh) * p.n_chunks * 2 * D;
         float a = 0.f, b2 = 0.f;
-        for (int c = 0; c < p.n_chunks; ++c) {
-            a += src[c * 2 * D + tid];
-            b2 += src[c * 2 * D + D + tid];
+        // ascending chunk order; eight chunks' partials are loaded before they are added
+        constexpr int FOLD = 8;
+        for (int c0 = 0; c0 < p.n_chunks; c0 += FOLD) {
+            float pa[FOLD], pb[FOLD];
+#pragma unroll
+            for (int j = 0; j < FOLD; ++j) {
+                const int c = min(c0 + j, p.n_chunks - 1);
+                pa[j] = src[c * 2 * D + tid];
+                pb[j] = src[c * 2 * D + D + tid];
+            }
+#pragma unroll
+            for (int j = 0; j < FOLD; ++j) {
+                if (c0 + j < p.n_chunks) {
+                    a += pa[j];
+                    b2 += pb[j];
+                }
+            }
         }
         mu = a / static_cast<float>(p.n_samples);
         var = fmaxf(b2 * inv_t - mu * mu, 0.f);

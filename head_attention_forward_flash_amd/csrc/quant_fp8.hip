@@ -5,7 +5,7 @@
 // hd128) and "MHA v4: fixes, refactor, new kernel, perf tweaks" (BF16/FP8
 // recipe, quantisation producers).
 //
-// One workgroup per (tensor, batch, head, block of 128 tokens):
+// One workgroup per (tensor, batch, block of 128 tokens, head):
 //   x      = fp32(bf16 input)                 (K: fp32(K) - mean[b, h, c], one fp32 rounding)
 //   amax   = max |x| over the block's tokens and channels (wave max, then LDS)
 //   scale  = amax / 448 in fp32 (1 when amax == 0)
@@ -27,14 +27,17 @@ namespace {
 constexpr int NT = 256;
 constexpr int TOK = 128;
 
+// Workgroup ids run over heads fastest, then token blocks, then batches: workgroups that are
+// dispatched together read neighbouring 2*D-byte pieces of the same BSHD token rows.
 template <int D>
-__device__ __forceinline__ void quant_block(const QuantParams& p, int bh_blk, float* red) {
+__device__ __forceinline__ void quant_block(const QuantParams& p, int id, float* red) {
     constexpr int TPR = D / 8;          // threads per token row (16 B each)
     constexpr int ROWS = NT / TPR;      // token rows per pass
     constexpr int PASSES = TOK / ROWS;
-    const int blk = bh_blk % p.nblk;
-    const int bh = bh_blk / p.nblk;
-    const int h = bh % p.heads, bb = bh / p.heads;
+    const int h = id % p.heads;
+    const int blk = (id / p.heads) % p.nblk;
+    const int bb = id / (p.heads * p.nblk);
+    const int bh = bb * p.heads + h;
     const int tid = threadIdx.x;
     const int c0 = (tid % TPR) * 8;
     const int r0 = tid / TPR;

@@ -29,8 +29,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
-PAGES_MLA_US = 4083.2         # the pages' tuned Triton time for the MLA-prefill workload (gfx950)
-PAGES_FP8_CALL_US = 219.2     # the pages' eager mha_v4 FP8 hd128 b1 h16 s4096 call (MI355X)
+# The pages' own times for the same shapes: the retune page's tuned Triton kernel (gfx950) for
+# the bf16 shapes, the gate page's eager mha_v4 call (MI355X) for the FP8 ones.
+PAGES_BF16_US = {"mla_d192_d128_causal": 4083.2, "mla_d192_d128_noncausal": 7086.1,
+                 "gqa_d128_8192_causal": 2686.6, "gqa_d64_causal": 333.0}
+PAGES_FP8_CALL_US = {"fp8_ksmooth_d128": 219.2, "fp8_long_h5": 3857.2}
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_mla_d192_d128_causal_traffic.json")
 KERNEL_SOURCES = ["head_attention_forward_flash_amd/csrc/attn_fwd_bf16.hip",
@@ -57,10 +60,21 @@ def traffic_bytes():
     return float(t["hbm_bytes_per_launch"])
 
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, min_warm_s=0.3):
+    """Average device time per call over exactly `steps` calls (HIP events on `stream`).
+
+    Warm-up is at least `warmup` calls and at least `min_warm_s` seconds of calls, so
+    that short kernels are timed at the clock the GPU settles to under load, not while
+    it ramps up.
+    """
     import torch
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t_warm < min_warm_s:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -102,12 +116,12 @@ def cpu_baseline(w, q, k, v, budget_s=12.0, max_heads=64):
             "seconds": round(elapsed, 2)}
 
 
-def bench_fp8(steps, warmup, dev):
-    """k_smooth_mean + mha_fwd_fp8 on the FP8 workload; None when the fp8 kernel is not built."""
+def bench_fp8(steps, warmup, dev, name="fp8_ksmooth_d128"):
+    """k_smooth_mean + mha_fwd_fp8 on an FP8 workload; None when the fp8 kernel is not built."""
     import torch
     import head_attention_forward_flash_amd as mha
     import workloads
-    w = workloads.WORKLOADS["fp8_ksmooth_d128"]
+    w = workloads.WORKLOADS[name]
     q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
     o = torch.empty((w.b, w.sq, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mha.mha_fwd_fp8_workspace_bytes(w.b, w.hq, w.hk, w.sq, w.sk, w.d_qk), dtype=torch.uint8,
@@ -128,7 +142,7 @@ def bench_fp8(steps, warmup, dev):
     ms, _ = time_launches(call, steps, warmup, stream)
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"available": True, "workload": w.name, "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 1),
-            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "pages_us_per_call": PAGES_FP8_CALL_US,
+            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "pages_us_per_call": PAGES_FP8_CALL_US.get(w.name),
             "includes": "k_smooth_mean (2 kernels) + quantisation + fp8 attention, device time by HIP events"}
 
 
@@ -140,6 +154,8 @@ def main():
     ap.add_argument("--workload", default="mla_d192_d128_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--fp8-workload", default="fp8_ksmooth_d128", help="FP8 workload of the fp8_call field")
+    ap.add_argument("--fp8-only", action="store_true", help="time only the quantised call; print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     a = ap.parse_args()
 
@@ -167,6 +183,9 @@ def main():
 
     import head_attention_forward_flash_amd as mha
     import workloads
+    if a.fp8_only:
+        print(json.dumps(bench_fp8(max(20, a.steps), a.warmup, dev, a.fp8_workload)), flush=True)
+        return
     w = workloads.WORKLOADS[a.workload]
     if w.fp8:
         print("--workload must be a bf16 workload", file=sys.stderr)
@@ -189,10 +208,10 @@ def main():
                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": None if traffic is None else int(traffic)}
 
-    fp8 = None if a.no_fp8 else bench_fp8(max(20, a.steps), a.warmup, dev)
+    fp8 = None if a.no_fp8 else bench_fp8(max(20, a.steps), a.warmup, dev, a.fp8_workload)
     cpu = None if a.no_cpu_baseline else cpu_baseline(w, qc, kc, vc)
 
-    pages_tflops = w.flops() / (PAGES_MLA_US * 1e-6) / 1e12 if w.name == "mla_d192_d128_causal" else None
+    pages_tflops = w.flops() / (PAGES_BF16_US[w.name] * 1e-6) / 1e12 if w.name in PAGES_BF16_US else None
     out = {
         "metric": "attention fwd TFLOP/s (causal-halved) and % of MI355X MFMA peak per config",
         "value": round(tflops, 1),

@@ -82,6 +82,19 @@ def test_full_mla_d192_d128_causal_sampled():
     _full_size_sampled("mla_d192_d128_causal", [0, 77, 127], 160, 9)
 
 
+def test_full_mla_d192_d128_noncausal_sampled():
+    _full_size_sampled("mla_d192_d128_noncausal", [0, 64, 127], 128, 10)
+
+
+def test_full_gqa_d128_8192_causal_sampled():
+    # heads 15 and 16 sit on either side of a kv-head boundary (16 query heads per kv head)
+    _full_size_sampled("gqa_d128_8192_causal", [0, 15, 16, 127], 128, 11)
+
+
+def test_full_mla_tp8_causal_sampled():
+    _full_size_sampled("mla_d192_d128_tp8_causal", [0, 15], 160, 12)
+
+
 def test_value_ones_gives_ones():
     # V = 1 everywhere: every output row is 1 whatever the scores, up to the bf16 rounding of
     # the probabilities fed to the P.V product and of O itself.

@@ -76,19 +76,22 @@ def test_quantised_codes_and_scales_bit_exact(smooth):
     assert (pad["q"] == 0).all() and (pad["k"] == 0).all(), "token padding must be zero codes"
 
 
-def _check_attention(q, k, v, mu, causal, what, heads=None):
+def _check_attention(q, k, v, mu, causal, what, heads=None, rows=None):
     o, lse, _, _ = _fp8_call(q, k, v, mu, causal)
     d = q.shape[3]
     o_ref, lse_ref, _ = oracle.fp8_attention_forward(q.float().numpy(), k.float().numpy(), v.float().numpy(),
-                                                     mu=mu, scale=d ** -0.5, causal=causal, heads=heads)
+                                                     mu=mu, scale=d ** -0.5, causal=causal, heads=heads,
+                                                     rows=rows)
     o_g = o.float().numpy().astype(np.float64)
     l_g = lse.numpy().astype(np.float64)
     if heads is not None:
         o_g, l_g = o_g[:, :, heads], l_g[:, heads]
+    if rows is not None:
+        o_g, l_g = o_g[:, rows], l_g[:, :, rows]
     rel = _rel_l2(o_g, o_ref)
     lerr = float(np.abs(l_g - lse_ref).max())
     exact, _ = oracle.attention_forward(q.float().numpy(), k.float().numpy(), v.float().numpy(),
-                                        scale=d ** -0.5, causal=causal, heads=heads)
+                                        scale=d ** -0.5, causal=causal, heads=heads, rows=rows)
     print(f"[fp8] {what}: rel_l2 vs same-quantisation oracle {rel:.3e}, vs unquantised {_rel_l2(o_g, exact):.3e}, "
           f"lse max-abs {lerr:.3e}", flush=True)
     assert rel <= FP8_REL_L2, f"{what}: rel-L2 {rel:.4e} > {FP8_REL_L2}"
@@ -111,6 +114,15 @@ def test_full_fp8_workload_sampled_heads():
     q, k, v = workloads.make_qkv(w)
     mu = _oracle_mu(k)
     _check_attention(q, k, v, mu, w.causal, "fp8 workload", heads=[0, 7, 15])
+
+
+def test_long_context_fp8_sampled():
+    # b1 h5 65536^2: 512 K/V scale blocks per head; sampled rows of the first and last head
+    w = workloads.WORKLOADS["fp8_long_h5"]
+    q, k, v = workloads.make_qkv(w)
+    mu = _oracle_mu(k)
+    rows = workloads.sample_indices(w.sq, 96, 13, include=[0, 127, 128, w.sq // 2, w.sq - 1])
+    _check_attention(q, k, v, mu, w.causal, "fp8 long context", heads=[0, 4], rows=rows)
 
 
 def test_gpu_gate_then_fp8_matches_oracle_pipeline():

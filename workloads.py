@@ -69,6 +69,24 @@ WORKLOADS = {
         "fp8_ksmooth_d128", b=1, hq=16, hk=16, sq=4096, sk=4096, d_qk=128, d_v=128, causal=False,
         seed=105, fp8=True, k_bias_std=3.0,
         description="b1 h16 4096^2 d128 non-causal, bf16 in, K smoothed, e4m3 compute, bf16 out"),
+    # Further shapes the pages time: the MLA shape without the causal mask and the d128
+    # hq128/hk8 8192^2 causal shape (the retune page's fixed-shape table; its batch is not
+    # printed, b = 1 here), one GPU's share of the MLA shape under 8-way head sharding, and
+    # the long-context FP8 call (the gate page's Performance table; causality not printed,
+    # non-causal here as for the h16 shape).
+    "mla_d192_d128_noncausal": Workload(
+        "mla_d192_d128_noncausal", b=1, hq=128, hk=128, sq=8192, sk=8192, d_qk=192, d_v=128, causal=False,
+        seed=106, description="b1 hq128 hk128 8192^2 dqk192 dv128 non-causal bf16"),
+    "gqa_d128_8192_causal": Workload(
+        "gqa_d128_8192_causal", b=1, hq=128, hk=8, sq=8192, sk=8192, d_qk=128, d_v=128, causal=True,
+        seed=107, description="b1 hq128 hk8 8192^2 d128 causal bf16"),
+    "mla_d192_d128_tp8_causal": Workload(
+        "mla_d192_d128_tp8_causal", b=1, hq=16, hk=16, sq=8192, sk=8192, d_qk=192, d_v=128, causal=True,
+        seed=108, description="b1 hq16 hk16 8192^2 dqk192 dv128 causal bf16 (one rank of 8-way head sharding)"),
+    "fp8_long_h5": Workload(
+        "fp8_long_h5", b=1, hq=5, hk=5, sq=65536, sk=65536, d_qk=128, d_v=128, causal=False,
+        seed=109, fp8=True, k_bias_std=3.0,
+        description="b1 h5 65536^2 d128 non-causal, bf16 in, K smoothed, e4m3 compute, bf16 out"),
 }
 
 

@@ -7,9 +7,11 @@ the tensors are not on a ROCm device the calls raise.
 
 Entry points (same names as the C ABI):
     mha_fwd_bf16(q, k, v, causal=False, softmax_scale=None, out=None, lse=True)
+    mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False, ...)
     k_smooth_mean(k, key_stride=1, max_keys=0, tau=0.25)
     mha_fwd_fp8(q, k, v, k_mean=None, causal=False, softmax_scale=None, out=None, lse=True)
-Tensors are BSHD views with a contiguous channel dimension.
+Tensors are BSHD views (varlen: THD, sequences packed along the token axis) with a
+contiguous channel dimension.
 """
 
 from __future__ import annotations
@@ -29,7 +31,7 @@ STATUS_NAMES = {
 
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = (
-    "mha_fwd_bf16", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
+    "mha_fwd_bf16", "mha_fwd_bf16_varlen", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_status_string", "mha_last_error",
 )
 
@@ -60,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_fwd_bf16.restype = i32
     lib.mha_fwd_bf16.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
                                  i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.mha_fwd_bf16_varlen.restype = i32
+    lib.mha_fwd_bf16_varlen.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.k_smooth_mean_workspace_bytes.restype = sz
     lib.k_smooth_mean_workspace_bytes.argtypes = [i32] * 6
     lib.k_smooth_mean.restype = i32
@@ -134,6 +139,46 @@ def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] =
     _check(lib.mha_fwd_bf16(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
                             _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
                             float(softmax_scale), int(bool(causal)), _stream(q.device)))
+    return out, lse_t
+
+
+def _thd_strides(t) -> Strides:
+    if t.dim() != 3:
+        raise ValueError(f"expected a 3-d THD tensor [tokens, heads, d], got shape {tuple(t.shape)}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("the channel dimension must be contiguous (stride 1)")
+    return Strides(0, t.stride(0), t.stride(1))
+
+
+def mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                        causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse: bool = True):
+    """Attention forward over packed sequences. q [total_q, hq, d_qk], k/v [total_k, hk, d],
+    cu_seqlens_* int32 [b + 1] on the device. Returns (o [total_q, hq, d_v], lse [hq, total_q] fp32 or None)."""
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, out, cu_seqlens_q, cu_seqlens_k)
+    total_q, hq, d_qk = q.shape
+    total_k, hk, _ = k.shape
+    d_v = v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-d int32 tensor")
+    b = cu_seqlens_q.numel() - 1
+    if b < 0 or cu_seqlens_k.numel() != b + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold b + 1 offsets")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((total_q, hq, d_v), dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty((hq, total_q), dtype=torch.float32, device=q.device) if lse else None
+    _check(lib.mha_fwd_bf16_varlen(_ptr(q), _thd_strides(q), _ptr(k), _thd_strides(k), _ptr(v), _thd_strides(v),
+                                   _ptr(out), _thd_strides(out), _ptr(lse_t), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), b, hq, hk, total_q, total_k, int(max_seqlen_q),
+                                   int(max_seqlen_k), d_qk, d_v, float(softmax_scale), int(bool(causal)),
+                                   _stream(q.device)))
     return out, lse_t
 
 

@@ -87,7 +87,7 @@ template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
 
-template <int DQK, int DV, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
     constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
@@ -138,10 +138,36 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     const int bb = bh / p.hq;
     const int g = h / p.group;
 
-    const char* qbase = static_cast<const char*>(p.q) + 2 * (bb * p.qv.sb + h * p.qv.sh);
-    const char* kbase = static_cast<const char*>(p.k) + 2 * (bb * p.kv.sb + g * p.kv.sh);
-    const char* vbase = static_cast<const char*>(p.v) + 2 * (bb * p.vv.sb + g * p.vv.sh);
-    const auto qrs = make_rsrc(qbase, p.qv.slice_bytes);
+    // ---- this workgroup's sequence: the whole batch row, or (varlen) packed tokens
+    //      [q0, q0 + sq) and [k0, k0 + sk) of the token axis.  Offsets are clamped to the
+    //      packed extent and the lengths to the declared maxima, so inconsistent offsets
+    //      can give wrong values but no access outside the tensors.
+    int sq = p.sq, sk = p.sk;
+    int64_t qrow0 = static_cast<int64_t>(bb) * p.qv.sb, krow0 = static_cast<int64_t>(bb) * p.kv.sb;
+    int64_t vrow0 = static_cast<int64_t>(bb) * p.vv.sb, orow0 = static_cast<int64_t>(bb) * p.ov.sb;
+    int64_t lse0 = (static_cast<int64_t>(bb) * p.hq + h) * p.sq;
+    uint32_t qslice = p.qv.slice_bytes, kslice = p.kv.slice_bytes, vslice = p.vv.slice_bytes;
+    if constexpr (VARLEN) {
+        const int qa = min(max(p.cu_q[bb], 0), p.total_q);
+        const int qe = min(max(p.cu_q[bb + 1], qa), p.total_q);
+        const int ka = min(max(p.cu_k[bb], 0), p.total_k);
+        const int ke = min(max(p.cu_k[bb + 1], ka), p.total_k);
+        sq = min(qe - qa, p.sq);
+        sk = min(ke - ka, p.sk);
+        if (mblk * BM >= sq) return;   // the whole workgroup: past this sequence's rows
+        qrow0 = static_cast<int64_t>(qa) * p.qv.ss;
+        orow0 = static_cast<int64_t>(qa) * p.ov.ss;
+        krow0 = static_cast<int64_t>(ka) * p.kv.ss;
+        vrow0 = static_cast<int64_t>(ka) * p.vv.ss;
+        lse0 = static_cast<int64_t>(h) * p.total_q + qa;
+        qslice = static_cast<uint32_t>((static_cast<int64_t>(sq - 1) * p.qv.ss + DQK) * 2);
+        kslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.kv.ss + DQK) * 2) : 0u;
+        vslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.vv.ss + DV) * 2) : 0u;
+    }
+    const char* qbase = static_cast<const char*>(p.q) + 2 * (qrow0 + h * p.qv.sh);
+    const char* kbase = static_cast<const char*>(p.k) + 2 * (krow0 + g * p.kv.sh);
+    const char* vbase = static_cast<const char*>(p.v) + 2 * (vrow0 + g * p.vv.sh);
+    const auto qrs = make_rsrc(qbase, qslice);
 
     const int wave_row0 = mblk * BM + wave * 32;
     const int my_row = wave_row0 + col;
@@ -149,7 +175,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[my_row][kk*16 + half*8 .. +8]
     bf16x8 qf[KSTEPS];
     {
-        const uint32_t rowoff = my_row < p.sq ? static_cast<uint32_t>(my_row * p.qv.ss * 2) : kOutOfRange;
+        const uint32_t rowoff = my_row < sq ? static_cast<uint32_t>(my_row * p.qv.ss * 2) : kOutOfRange;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
@@ -161,7 +187,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     }
     const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
 
-    const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
+    const int kv_end = CAUSAL ? min(sk, (mblk + 1) * BM) : sk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
     // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
@@ -191,20 +217,19 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
         const int r = pos / VROWB, pc = (pos % VROWB) / 16;
         vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
     }
-    auto tile_rsrc = [&](const char* base, const View& vw, int t) __attribute__((always_inline)) {
+    auto tile_rsrc = [&](const char* base, const View& vw, uint32_t slice, int t) __attribute__((always_inline)) {
         const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
-        const uint32_t left = start < static_cast<int64_t>(vw.slice_bytes)
-                                  ? static_cast<uint32_t>(vw.slice_bytes - start) : 0u;
+        const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
         return make_rsrc(left ? base + start : base, left);
     };
     // past the last tile the buffer range is empty: nothing is read
     auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-        const auto r = tile_rsrc(kbase, p.kv, t);
+        const auto r = tile_rsrc(kbase, p.kv, kslice, t);
 #pragma unroll
         for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
     };
     auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-        const auto r = tile_rsrc(vbase, p.vv, t);
+        const auto r = tile_rsrc(vbase, p.vv, vslice, t);
 #pragma unroll
         for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
     };
@@ -255,13 +280,13 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     // ---- scores of keys past sk, or above the diagonal, become -inf (block u = keys 32u ..)
     auto need_mask = [&](int u) __attribute__((always_inline)) {
         const int key0 = u * 32;
-        return (key0 + 32 > p.sk) || (CAUSAL && key0 + 31 > wave_row0);
+        return (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
     };
     auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-            if (key >= p.sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
+            if (key >= sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
         }
     };
     // ---- this lane's max over its 16 scores of a block
@@ -448,8 +473,8 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     // ---- epilogue: normalise, store O (bf16) and LSE
     const float l_tot = l_run + swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_row < p.sq) {
-        uint16_t* orow = static_cast<uint16_t*>(p.o) + (bb * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss);
+    if (my_row < sq) {
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + (orow0 + h * p.ov.sh + my_row * p.ov.ss);
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) {
 #pragma unroll
@@ -462,32 +487,39 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
         }
         if (p.lse != nullptr && half == 0) {
             const float lse = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
-            p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
+            p.lse[lse0 + my_row] = lse;
         }
     }
 }
 
-template <int DQK, int DV, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN>
 hipError_t launch(AttnParams p, hipStream_t stream) {
     constexpr int BM = TileCfg<DQK, DV>::BM;
     p.n_mblocks = (p.sq + BM - 1) / BM;
     const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
     if (nwg == 0) return hipSuccess;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL>), dim3(static_cast<unsigned>(nwg)),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN>), dim3(static_cast<unsigned>(nwg)),
                        dim3(BM * 2), 0, stream, p);
     return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t launch_dims(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
+    if (d_qk == 64 && d_v == 64)
+        return causal ? launch<64, 64, true, VARLEN>(p, stream) : launch<64, 64, false, VARLEN>(p, stream);
+    if (d_qk == 128 && d_v == 128)
+        return causal ? launch<128, 128, true, VARLEN>(p, stream) : launch<128, 128, false, VARLEN>(p, stream);
+    if (d_qk == 192 && d_v == 128)
+        return causal ? launch<192, 128, true, VARLEN>(p, stream) : launch<192, 128, false, VARLEN>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
-    if (d_qk == 64 && d_v == 64) return causal ? launch<64, 64, true>(p, stream) : launch<64, 64, false>(p, stream);
-    if (d_qk == 128 && d_v == 128)
-        return causal ? launch<128, 128, true>(p, stream) : launch<128, 128, false>(p, stream);
-    if (d_qk == 192 && d_v == 128)
-        return causal ? launch<192, 128, true>(p, stream) : launch<192, 128, false>(p, stream);
-    return hipErrorInvalidValue;
+    return p.cu_q != nullptr ? launch_dims<true>(p, d_qk, d_v, causal, stream)
+                             : launch_dims<false>(p, d_qk, d_v, causal, stream);
 }
 
 }  // namespace mha

@@ -24,6 +24,12 @@ struct AttnParams {
     int group;       // hq / hk
     int n_mblocks;   // ceil(sq / rows per workgroup), set by the launcher
     float scale_log2;  // softmax_scale * log2(e)
+    // packed sequences (varlen): b sequences, sequence i owning query tokens
+    // [cu_q[i], cu_q[i+1]) and key tokens [cu_k[i], cu_k[i+1]) of a token axis of
+    // total_q / total_k rows; sq / sk are then the maximum lengths.  cu_q == nullptr: dense.
+    const int* cu_q = nullptr;
+    const int* cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 // bf16 attention forward: d_qk/d_v in {(64,64), (128,128), (192,128)}.

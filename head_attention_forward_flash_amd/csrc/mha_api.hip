@@ -160,6 +160,66 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
                       "attn_fwd_bf16 launch");
 }
 
+mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                               const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int b, int hq, int hk,
+                               int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
+                               float softmax_scale, int causal, void* stream) {
+    if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(MHA_ERR_SHAPE, "total_q, total_k, max_seqlen_q, max_seqlen_k must be >= 0 (%d %d %d %d)",
+                    total_q, total_k, max_seqlen_q, max_seqlen_k);
+    mha_status st = check_common(b, hq, hk, max_seqlen_q, max_seqlen_k, softmax_scale, causal);
+    if (st != MHA_OK) return st;
+    if (!supported_bf16(d_qk, d_v))
+        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (64,64) (128,128) (192,128)",
+                    d_qk, d_v);
+    const bool has_rows = b > 0 && total_q > 0 && max_seqlen_q > 0;
+    if (b > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(MHA_ERR_NULL, "cu_seqlens_q / cu_seqlens_k is NULL");
+    if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 || reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4)
+        return fail(MHA_ERR_LAYOUT, "cu_seqlens arrays must be 4-byte aligned");
+    if (has_rows && !q) return fail(MHA_ERR_NULL, "q is NULL");
+    if (has_rows && total_k > 0 && !k) return fail(MHA_ERR_NULL, "k is NULL");
+    if (has_rows && total_k > 0 && !v) return fail(MHA_ERR_NULL, "v is NULL");
+    if (has_rows && !o) return fail(MHA_ERR_NULL, "o is NULL");
+    if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MHA_ERR_LAYOUT, "lse must be 4-byte aligned");
+    if (int64_t(hq) * total_q > INT32_MAX) return fail(MHA_ERR_OVERFLOW, "hq * total_q exceeds 2^31-1");
+
+    // The packed token axis plays the role of one batch row: the batch stride is ignored.
+    auto packed = [](mha_strides s) { return mha_strides{0, s.s, s.h}; };
+    mha::AttnParams p{};
+    if ((st = make_view("q", q, packed(q_stride), hq, total_q, d_qk, 2, true, &p.qv)) != MHA_OK) return st;
+    if ((st = make_view("k", k, packed(k_stride), hk, total_k, d_qk, 2, true, &p.kv)) != MHA_OK) return st;
+    if ((st = make_view("v", v, packed(v_stride), hk, total_k, d_v, 2, true, &p.vv)) != MHA_OK) return st;
+    if ((st = make_view("o", o, packed(o_stride), hq, total_q, d_v, 2, true, &p.ov)) != MHA_OK) return st;
+    if (total_k > 1 && k_stride.s < d_qk)
+        return fail(MHA_ERR_LAYOUT, "k: rows overlap (stride.s = %lld < d_qk = %d)", (long long)k_stride.s, d_qk);
+    if (total_k > 1 && v_stride.s < d_v)
+        return fail(MHA_ERR_LAYOUT, "v: rows overlap (stride.s = %lld < d_v = %d)", (long long)v_stride.s, d_v);
+
+    const int64_t nwg = int64_t(b) * hq * ((int64_t(max_seqlen_q) + 127) / 128);
+    if (nwg > INT32_MAX) return fail(MHA_ERR_OVERFLOW, "grid of %lld workgroups exceeds 2^31-1", (long long)nwg);
+    if (!has_rows) return ok();
+
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.b = b;
+    p.hq = hq;
+    p.hk = hk;
+    p.sq = max_seqlen_q;
+    p.sk = max_seqlen_k;
+    p.group = hq / hk;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
+                      "attn_fwd_bf16 (varlen) launch");
+}
+
 size_t k_smooth_mean_workspace_bytes(int b, int hk, int sk, int d, int key_stride, int max_keys) {
     if (b < 0 || hk < 1 || sk < 0 || d < 1 || key_stride < 1 || max_keys < 0) return 0;
     int64_t t = sk > 0 ? (int64_t(sk) + key_stride - 1) / key_stride : 0;

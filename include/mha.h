@@ -97,6 +97,39 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride,
                         float softmax_scale, int causal, void* stream);
 
 /*
+ * mha_fwd_bf16_varlen - mha_fwd_bf16 over a batch of packed sequences of
+ * different lengths: the "varlen" layout the retuned Triton MHA forward is
+ * timed in next to BSHD ("Tune MHA config & small-head pipeline pathology",
+ * Test Plan and the per-shape tables' layout column).
+ *
+ *   q    [total_q, hq, d_qk] bf16      k [total_k, hk, d_qk] bf16
+ *   v    [total_k, hk, d_v]  bf16      o [total_q, hq, d_v]  bf16 (written)
+ *   lse  [hq, total_q] fp32 contiguous (written), or NULL
+ *   cu_seqlens_q, cu_seqlens_k: device int32 arrays of b + 1 entries; sequence
+ *        i owns query tokens [cu_seqlens_q[i], cu_seqlens_q[i+1]) and key tokens
+ *        [cu_seqlens_k[i], cu_seqlens_k[i+1]).  The caller guarantees
+ *        0 = cu[0] <= cu[1] <= ... <= cu[b] = total and that every length is
+ *        at most max_seqlen_q / max_seqlen_k (query rows past max_seqlen_q would
+ *        be left unwritten).  The kernel clamps offsets to [0, total] and lengths
+ *        to the maxima, so inconsistent arrays give wrong values but never an
+ *        access outside q, k, v, o or lse.
+ *   A sequence without keys gives O = 0 and LSE = -inf on its rows.
+ *   causal: within a sequence, key j is visible to query i iff j <= i (top-left).
+ *   Strides: token stride .s and head stride .h; .b is ignored.  Layout and
+ *   size rules as mha_fwd_bf16 with the packed token axis as the one batch row
+ *   (the whole packed tensor must span < 2^31 bytes per head).
+ */
+mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride,
+                               const void* k, mha_strides k_stride,
+                               const void* v, mha_strides v_stride,
+                               void* o, mha_strides o_stride,
+                               float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int b, int hq, int hk, int total_q, int total_k,
+                               int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
+                               float softmax_scale, int causal, void* stream);
+
+/*
  * k_smooth_mean - the K-smoothing gate of "[HIP] Mha v4: run the K-smoothing
  * gate as one HIP call" (Summary; commit message): per-(batch*kv head, chunk)
  * moments over a strided key sample, then a per-head fold and a threshold,

@@ -20,7 +20,8 @@ Sources (web pages; cited by title and section):
 
 Modules:
   attention  - softmax(scale * Q K^T + causal mask) V with GQA, and the
-               per-row log-sum-exp (plain definition).
+               per-row log-sum-exp (plain definition); the same over packed
+               sequences of different lengths (varlen).
   gate       - K-smoothing gate: strided key sample, per-channel moments,
                gate decision, mean output (the algorithm's steps).
   fp8        - OCP E4M3 rounding, per-128-token-block scaling, and attention
@@ -32,7 +33,7 @@ outside this package: closed forms, hand-derived examples under
 torch's float8_e4m3fn cast, numpy's mean/var) and brute force.
 """
 
-from .attention import attention_forward, attention_flops  # noqa: F401
+from .attention import attention_forward, attention_flops, attention_varlen  # noqa: F401
 from .gate import k_smooth_mean, key_sample  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,

@@ -87,3 +87,39 @@ def attention_forward(q, k, v, *, scale, causal, heads=None, rows=None, batches=
             with np.errstate(divide="ignore"):
                 lse[bi, hi, :] = np.where(has_key, m_safe + np.log(np.where(has_key, l, 1.0)), -np.inf)
     return o, lse
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, *, scale, causal, heads=None, rows=None):
+    """Attention forward over packed sequences (the "varlen" layout), float64.
+
+    q: [total_q, hq, d_qk], k: [total_k, hk, d_qk], v: [total_k, hk, d_v] (THD);
+    cu_q, cu_k: b + 1 offsets; sequence i owns query tokens cu_q[i]..cu_q[i+1]-1
+    and key tokens cu_k[i]..cu_k[i+1]-1, and its rows attend to its own keys only,
+    exactly as ``attention_forward`` on that sequence alone (top-left causal
+    mask in the sequence's own positions).  heads / rows: optional index lists
+    (rows index the packed token axis).
+
+    Returns (o [nrows, nheads, d_v], lse [nheads, nrows]), both float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    total_q, hq, _ = q.shape
+    d_v = v.shape[2]
+    heads = list(range(hq)) if heads is None else list(heads)
+    rows = list(range(total_q)) if rows is None else list(rows)
+    o = np.zeros((len(rows), len(heads), d_v), dtype=np.float64)
+    lse = np.full((len(heads), len(rows)), -np.inf, dtype=np.float64)
+    for i in range(len(cu_q) - 1):
+        qa, qe, ka, ke = cu_q[i], cu_q[i + 1], cu_k[i], cu_k[i + 1]
+        sel = [n for n, r in enumerate(rows) if qa <= r < qe]
+        if not sel:
+            continue
+        local = [rows[n] - qa for n in sel]
+        oi, li = attention_forward(q[None, qa:qe], k[None, ka:ke], v[None, ka:ke], scale=scale,
+                                   causal=causal, heads=heads, rows=local)
+        o[sel] = oi[0]
+        lse[:, sel] = li[0]
+    return o, lse

@@ -85,6 +85,42 @@ def test_bf16_empty_problem_is_a_noop(lib):
     assert _bf16(lib, b=0)[0] == 0
 
 
+def _varlen(lib, **kw):
+    a = dict(q=FAKE, qs=S(0, 2 * 64, 64), k=FAKE, ks=S(0, 2 * 64, 64), v=FAKE, vs=S(0, 2 * 64, 64),
+             o=FAKE, os=S(0, 2 * 64, 64), lse=None, cuq=FAKE, cuk=FAKE, b=3, hq=2, hk=2, tq=300, tk=300,
+             mq=128, mk=128, dqk=64, dv=64, scale=0.125, causal=1)
+    a.update(kw)
+    st = lib.mha_fwd_bf16_varlen(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"], a["lse"],
+                                 a["cuq"], a["cuk"], a["b"], a["hq"], a["hk"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                 a["dqk"], a["dv"], a["scale"], a["causal"], None)
+    return st, lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cuq=None), 1, "cu_seqlens"),
+    (dict(cuk=None), 1, "cu_seqlens"),
+    (dict(cuq=FAKE + 2), 4, "cu_seqlens arrays must be 4-byte aligned"),
+    (dict(tq=-1), 2, "total_q"),
+    (dict(mk=-5), 2, "max_seqlen"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(hq=3), 2, "multiple of hk"),
+    (dict(dqk=96, dv=96), 3, "not built"),
+    (dict(ks=S(0, 32, 16)), 4, "k: rows overlap"),
+    (dict(qs=S(0, 1 << 24, 64), tq=300), 5, "q: one (batch, head) slice"),
+    (dict(causal=3), 8, "causal"),
+])
+def test_varlen_refusals(lib, kw, status, needle):
+    st, msg = _varlen(lib, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_varlen_empty_problem_is_a_noop(lib):
+    assert _varlen(lib, b=0, cuq=None, cuk=None)[0] == 0
+    assert _varlen(lib, tq=0, q=None, o=None)[0] == 0
+    assert _varlen(lib, mq=0)[0] == 0
+
+
 def test_gate_refusals_and_workspace(lib):
     need = lib.k_smooth_mean_workspace_bytes(2, 3, 1000, 128, 1, 0)
     assert need >= 2 * 3 * 4 * 2 * 128 * 4 and need % 256 == 0

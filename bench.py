@@ -146,6 +146,28 @@ def bench_fp8(steps, warmup, dev, name="fp8_ksmooth_d128"):
             "includes": "k_smooth_mean (2 kernels) + quantisation + fp8 attention, device time by HIP events"}
 
 
+def bench_varlen(steps, warmup, dev, name):
+    """mha_fwd_bf16_varlen on a packed-sequence workload."""
+    import itertools
+    import torch
+    import head_attention_forward_flash_amd as mha
+    import workloads
+    w = workloads.VARLEN_WORKLOADS[name]
+    lens = w.lengths()
+    q, k, v = (t.to(dev) for t in w.make_qkv())
+    cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=dev)
+    o = torch.empty((q.shape[0], w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        mha.mha_fwd_bf16_varlen(q, k, v, cu, cu, max(lens), max(lens), causal=w.causal, out=o, lse=False)
+
+    ms, _ = time_launches(call, steps, warmup, stream)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "sequences": len(lens), "tokens": sum(lens), "us_per_launch": round(ms * 1e3, 1),
+            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +178,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-workload", default="fp8_ksmooth_d128", help="FP8 workload of the fp8_call field")
     ap.add_argument("--fp8-only", action="store_true", help="time only the quantised call; print its JSON")
+    ap.add_argument("--varlen-workload", default=None, help="time only this packed-sequence workload; print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     a = ap.parse_args()
 
@@ -183,6 +206,9 @@ def main():
 
     import head_attention_forward_flash_amd as mha
     import workloads
+    if a.varlen_workload:
+        print(json.dumps(bench_varlen(a.steps, a.warmup, dev, a.varlen_workload)), flush=True)
+        return
     if a.fp8_only:
         print(json.dumps(bench_fp8(max(20, a.steps), a.warmup, dev, a.fp8_workload)), flush=True)
         return

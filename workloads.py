@@ -129,3 +129,48 @@ def sample_indices(n: int, count: int, seed: int, include=()) -> list:
     picked = set(int(i) for i in torch.randperm(n, generator=gen)[:count])
     picked.update(int(i) % n for i in include if n > 0)
     return sorted(picked)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed sequences (THD) of seeded lengths; FLOPs are summed per sequence."""
+    name: str
+    n_seq: int
+    min_len: int
+    max_len: int
+    hq: int
+    hk: int
+    d_qk: int
+    d_v: int
+    causal: bool
+    seed: int
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+    def lengths(self):
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(self.seed)
+        return [int(x) for x in torch.randint(self.min_len, self.max_len + 1, (self.n_seq,), generator=gen)]
+
+    def flops(self) -> float:
+        f = sum(2.0 * self.hq * n * n * (self.d_qk + self.d_v) for n in self.lengths())
+        return f / 2.0 if self.causal else f
+
+    def make_qkv(self):
+        total = sum(self.lengths())
+        q = make_random((total, self.hq, self.d_qk), self.seed + 1)
+        k = make_random((total, self.hk, self.d_qk), self.seed + 2)
+        v = make_random((total, self.hk, self.d_v), self.seed + 3)
+        return q, k, v
+
+
+# Packed-sequence prefill: 32 sequences of 512..8192 tokens, Llama-like GQA heads.
+VARLEN_WORKLOADS = {
+    "varlen_gqa_d128_causal": VarlenWorkload(
+        "varlen_gqa_d128_causal", n_seq=32, min_len=512, max_len=8192, hq=32, hk=8, d_qk=128, d_v=128,
+        causal=True, seed=110,
+        description="32 packed sequences of 512..8192 tokens, hq32 hk8 d128 causal bf16"),
+}

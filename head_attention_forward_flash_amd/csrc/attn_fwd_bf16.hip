@@ -6,7 +6,8 @@
 // dqk=192/dv=128 "pe" bucket; Profile 2: pipelining depth as the main lever).
 //
 // Work decomposition: one workgroup per (batch, query head, block of BM query
-// rows), one wave per 32 rows.  The kernel computes the TRANSPOSED scores
+// rows), one wave per 32 rows; causal grids that fill the device only a few
+// times give each workgroup the pair of blocks j and n-1-j instead.  The kernel computes the TRANSPOSED scores
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds one query row
 // (lane % 32) and half of the keys of each 32-key block: the row max and row sum
 // stay in the lane except for one exchange with lane ^ 32, and the probabilities
@@ -87,7 +88,7 @@ template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
 
-template <int DQK, int DV, bool CAUSAL, bool VARLEN>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
     constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
@@ -120,374 +121,401 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
         else return v_lds1;
     };
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 31;     // query column of this lane in S^T / O^T
-    const int half = lane >> 5;    // which half of the wave
-
-    // ---- workgroup -> (batch, head, query block); consecutive logical ids stay on one XCD
+    // ---- workgroup -> (batch, head, query block); consecutive logical ids stay on one XCD.
+    //      Causal attention on a grid of a few rounds pairs the query blocks of a head
+    //      (PAIRED): a workgroup takes block n-1-j and then block j, so every workgroup does
+    //      the same work and the grid has no tail of light workgroups.
+    static_assert(CAUSAL || !PAIRED, "only causal blocks differ in work");
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
     const int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
-    const int mrev = lid % p.n_mblocks;
-    const int bh = lid / p.n_mblocks;
-    const int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first
-    const int h = bh % p.hq;
-    const int bb = bh / p.hq;
-    const int g = h / p.group;
-
-    // ---- this workgroup's sequence: the whole batch row, or (varlen) packed tokens
-    //      [q0, q0 + sq) and [k0, k0 + sk) of the token axis.  Offsets are clamped to the
-    //      packed extent and the lengths to the declared maxima, so inconsistent offsets
-    //      can give wrong values but no access outside the tensors.
-    int sq = p.sq, sk = p.sk;
-    int64_t qrow0 = static_cast<int64_t>(bb) * p.qv.sb, krow0 = static_cast<int64_t>(bb) * p.kv.sb;
-    int64_t vrow0 = static_cast<int64_t>(bb) * p.vv.sb, orow0 = static_cast<int64_t>(bb) * p.ov.sb;
-    int64_t lse0 = (static_cast<int64_t>(bb) * p.hq + h) * p.sq;
-    uint32_t qslice = p.qv.slice_bytes, kslice = p.kv.slice_bytes, vslice = p.vv.slice_bytes;
-    if constexpr (VARLEN) {
-        const int qa = min(max(p.cu_q[bb], 0), p.total_q);
-        const int qe = min(max(p.cu_q[bb + 1], qa), p.total_q);
-        const int ka = min(max(p.cu_k[bb], 0), p.total_k);
-        const int ke = min(max(p.cu_k[bb + 1], ka), p.total_k);
-        sq = min(qe - qa, p.sq);
-        sk = min(ke - ka, p.sk);
-        if (mblk * BM >= sq) return;   // the whole workgroup: past this sequence's rows
-        qrow0 = static_cast<int64_t>(qa) * p.qv.ss;
-        orow0 = static_cast<int64_t>(qa) * p.ov.ss;
-        krow0 = static_cast<int64_t>(ka) * p.kv.ss;
-        vrow0 = static_cast<int64_t>(ka) * p.vv.ss;
-        lse0 = static_cast<int64_t>(h) * p.total_q + qa;
-        qslice = static_cast<uint32_t>((static_cast<int64_t>(sq - 1) * p.qv.ss + DQK) * 2);
-        kslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.kv.ss + DQK) * 2) : 0u;
-        vslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.vv.ss + DV) * 2) : 0u;
-    }
-    const char* qbase = static_cast<const char*>(p.q) + 2 * (qrow0 + h * p.qv.sh);
-    const char* kbase = static_cast<const char*>(p.k) + 2 * (krow0 + g * p.kv.sh);
-    const char* vbase = static_cast<const char*>(p.v) + 2 * (vrow0 + g * p.vv.sh);
-    const auto qrs = make_rsrc(qbase, qslice);
-
-    const int wave_row0 = mblk * BM + wave * 32;
-    const int my_row = wave_row0 + col;
-
-    // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[my_row][kk*16 + half*8 .. +8]
-    bf16x8 qf[KSTEPS];
+    const int per_head = PAIRED ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
+    const int mrev = lid % per_head;
+    const int bh = lid / per_head;
+    int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first
+    bool lds_zeroed = false;
+next_item:
+    // A pair's second block passes the lane index through an empty asm statement: nothing
+    // derived from it (fragment addresses, mask offsets) is then hoisted out of the loop over
+    // the pair, where it would stay live across every tile and crowd the tile loop's registers.
+    int tid = threadIdx.x;
+    if constexpr (PAIRED) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;     // query column of this lane in S^T / O^T
+    const int half = lane >> 5;    // which half of the wave
     {
-        const uint32_t rowoff = my_row < sq ? static_cast<uint32_t>(my_row * p.qv.ss * 2) : kOutOfRange;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
-            u32x4 w = buffer_load_b128(qrs, off);
-            // softmax(c * s) with c < 0 equals softmax(|c| * (-s)): negate Q (exact) and use |c|
-            if (p.scale_log2 < 0.f) w ^= 0x80008000u;
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-    const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
+        const int h = bh % p.hq;
+        const int bb = bh / p.hq;
+        const int g = h / p.group;
 
-    const int kv_end = CAUSAL ? min(sk, (mblk + 1) * BM) : sk;
-    const int ntiles = (kv_end + BN - 1) / BN;
-
-    // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
-    //      address decides what lands there.  The 16-byte chunks of a row are XOR-swizzled
-    //      so that the fragment reads are bank-conflict free on gfx950's LDS, which serves
-    //      256 bytes per clock (16 lanes of a b128 read, 32 lanes of a b64 read):
-    //        K: the 16 rows one b128 read touches land on 16 distinct 16-byte bank groups;
-    //        V: the 4 rows one transposing read touches land on 4 distinct 64-byte quarters.
-    //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
-    //      based at the tile and bounded by the slice, so keys past sk land as zeros.
-    auto kswz = [](int r) __attribute__((always_inline)) {
-        return KROWB % 256 == 0 ? (r & 15) : ((r >> 1) & 7);    // rows of 256 B, else 128/384 B
-    };
-    auto vswz = [](int r) __attribute__((always_inline)) {
-        return VROWB % 256 == 0 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
-    };
-    uint32_t kgo[KDMA], vgo[VDMA];
-#pragma unroll
-    for (int i = 0; i < KDMA; ++i) {
-        const int pos = (wave * KDMA + i) * 1024 + lane * 16;
-        const int r = pos / KROWB, pc = (pos % KROWB) / 16;
-        kgo[i] = static_cast<uint32_t>(r * p.kv.ss * 2 + ((pc ^ kswz(r)) * 16));
-    }
-#pragma unroll
-    for (int i = 0; i < VDMA; ++i) {
-        const int pos = (wave * VDMA + i) * 1024 + lane * 16;
-        const int r = pos / VROWB, pc = (pos % VROWB) / 16;
-        vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
-    }
-    auto tile_rsrc = [&](const char* base, const View& vw, uint32_t slice, int t) __attribute__((always_inline)) {
-        const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
-        const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
-        return make_rsrc(left ? base + start : base, left);
-    };
-    // past the last tile the buffer range is empty: nothing is read
-    auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-        const auto r = tile_rsrc(kbase, p.kv, kslice, t);
-#pragma unroll
-        for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
-    };
-    auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-        const auto r = tile_rsrc(vbase, p.vv, vslice, t);
-#pragma unroll
-        for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
-    };
-
-    // LDS starts as zeros so that any row the DMA does not fill holds finite values
-    for (int i = tid; i < KTILE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
-    }
-    for (int i = tid; i < VTILE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
-    }
-    __syncthreads();
-
-    f32x16 oacc[CBLK];
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
-    float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
-    float l_run = 0.f;       // this lane's partial row sum over its half of the keys
-
-    // fragment addresses inside a slot (bytes)
-    const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
-    const int t16 = lane & 15;
-    // V transposing reads: lane t of a 16-lane group points at key (k0 + t/4), channel
-    // (c0 + 4*(t%4)); the group then receives, lane by lane, 16 consecutive channels of 4 keys.
-    const int vkey_l = half * 4 + (t16 >> 2);                 // key offset inside a 16-key step
-    const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3); // channel offset inside a 32-block
-
-    // K fragment of k-step kk: row (kb*32 + col), 16-byte chunk (2*kk + half) ^ kx.  The swizzle
-    // only permutes chunks inside aligned groups of KSW chunks, so the address is one of
-    // KSW/2 per-lane offsets plus an immediate.
-    constexpr int KSW = KROWB % 256 == 0 ? 16 : 8;
-    uint32_t koff[KSW / 2];
-#pragma unroll
-    for (int j = 0; j < KSW / 2; ++j) koff[j] = col * KROWB + ((2 * j + half) ^ kx) * 16;
-
-    // ---- S^T = K Q^T for the 32-key block kb of a K tile (one accumulator)
-    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
-        s = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const uint8_t* a_ptr = kl + koff[kk % (KSW / 2)] + (kk / (KSW / 2)) * KSW * 16 + kb * 32 * KROWB;
-            const auto a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_ptr));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-        }
-    };
-    // ---- scores of keys past sk, or above the diagonal, become -inf (block u = keys 32u ..)
-    auto need_mask = [&](int u) __attribute__((always_inline)) {
-        const int key0 = u * 32;
-        return (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
-    };
-    auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-            if (key >= sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
-        }
-    };
-    // ---- this lane's max over its 16 scores of a block
-    auto lane_max = [&](const f32x16& s) __attribute__((always_inline)) {
-        float a = __builtin_fmaxf(s[0], s[1]);
-        float b = __builtin_fmaxf(s[14], s[15]);
-#pragma unroll
-        for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
-#pragma unroll
-        for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
-        return __builtin_fmaxf(a, b);
-    };
-    // ---- online softmax update from a block max (the reference max only moves when a row's
-    //      max grows by more than 2^8 in probability); returns m * c for the exponentials
-    auto softmax_update = [&](float mx) __attribute__((always_inline)) {
-        const float mt = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run, mt);
-        const bool grow = m_new > m_run && (m_run == kNegInf || (m_new - m_run) * c > kRescaleThreshold);
-        if (__any(grow)) {
-            const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-            m_run = m_new;
-        }
-        return m_run == kNegInf ? 0.f : m_run * c;
-    };
-    // ---- P^T = exp2(S^T c - m c) rounded to bf16, as the B operands of two 16-key P.V steps
-    auto exp_block = [&](const f32x16& s, float mc, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, -mc));
-                const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, -mc));
-                w[i] = pack_bf16x2(p0, p1);
+        // ---- this workgroup's sequence: the whole batch row, or (varlen) packed tokens
+        //      [q0, q0 + sq) and [k0, k0 + sk) of the token axis.  Offsets are clamped to the
+        //      packed extent and the lengths to the declared maxima, so inconsistent offsets
+        //      can give wrong values but no access outside the tensors.
+        int sq = p.sq, sk = p.sk;
+        int64_t qrow0 = static_cast<int64_t>(bb) * p.qv.sb, krow0 = static_cast<int64_t>(bb) * p.kv.sb;
+        int64_t vrow0 = static_cast<int64_t>(bb) * p.vv.sb, orow0 = static_cast<int64_t>(bb) * p.ov.sb;
+        int64_t lse0 = (static_cast<int64_t>(bb) * p.hq + h) * p.sq;
+        uint32_t qslice = p.qv.slice_bytes, kslice = p.kv.slice_bytes, vslice = p.vv.slice_bytes;
+        if constexpr (VARLEN) {
+            const int qa = min(max(p.cu_q[bb], 0), p.total_q);
+            const int qe = min(max(p.cu_q[bb + 1], qa), p.total_q);
+            const int ka = min(max(p.cu_k[bb], 0), p.total_k);
+            const int ke = min(max(p.cu_k[bb + 1], ka), p.total_k);
+            sq = min(qe - qa, p.sq);
+            sk = min(ke - ka, p.sk);
+            if (mblk * BM >= sq) {      // the whole workgroup: past this sequence's rows
+                if constexpr (PAIRED) goto item_done;
+                else return;
             }
-            pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            qrow0 = static_cast<int64_t>(qa) * p.qv.ss;
+            orow0 = static_cast<int64_t>(qa) * p.ov.ss;
+            krow0 = static_cast<int64_t>(ka) * p.kv.ss;
+            vrow0 = static_cast<int64_t>(ka) * p.vv.ss;
+            lse0 = static_cast<int64_t>(h) * p.total_q + qa;
+            qslice = static_cast<uint32_t>((static_cast<int64_t>(sq - 1) * p.qv.ss + DQK) * 2);
+            kslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.kv.ss + DQK) * 2) : 0u;
+            vslice = sk > 0 ? static_cast<uint32_t>((static_cast<int64_t>(sk - 1) * p.vv.ss + DV) * 2) : 0u;
         }
-    };
-    // ---- row sum of the rounded P fed to P.V
-    auto row_sum = [&](const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-        float a = 0.f;
+        const char* qbase = static_cast<const char*>(p.q) + 2 * (qrow0 + h * p.qv.sh);
+        const char* kbase = static_cast<const char*>(p.k) + 2 * (krow0 + g * p.kv.sh);
+        const char* vbase = static_cast<const char*>(p.v) + 2 * (vrow0 + g * p.vv.sh);
+        const auto qrs = make_rsrc(qbase, qslice);
+
+        const int wave_row0 = mblk * BM + wave * 32;
+        const int my_row = wave_row0 + col;
+
+        // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[my_row][kk*16 + half*8 .. +8]
+        bf16x8 qf[KSTEPS];
+        {
+            const uint32_t rowoff = my_row < sq ? static_cast<uint32_t>(my_row * p.qv.ss * 2) : kOutOfRange;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
+                u32x4 w = buffer_load_b128(qrs, off);
+                // softmax(c * s) with c < 0 equals softmax(|c| * (-s)): negate Q (exact) and use |c|
+                if (p.scale_log2 < 0.f) w ^= 0x80008000u;
+                qf[kk] = __builtin_bit_cast(bf16x8, w);
+            }
         }
-        l_run += a;
-    };
-    // ---- O^T += V^T P^T over the 32-key block kb of a V tile: the A operand (32 channels x
-    //      16 keys) comes from two transposing reads of row-major V; keys ks*16 +
-    //      {half*4 .. +3} and {8 + half*4 .. +3} match the key order of P^T's B operand
-    auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
+
+        const int kv_end = CAUSAL ? min(sk, (mblk + 1) * BM) : sk;
+        const int ntiles = (kv_end + BN - 1) / BN;
+
+        // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
+        //      address decides what lands there.  The 16-byte chunks of a row are XOR-swizzled
+        //      so that the fragment reads are bank-conflict free on gfx950's LDS, which serves
+        //      256 bytes per clock (16 lanes of a b128 read, 32 lanes of a b64 read):
+        //        K: the 16 rows one b128 read touches land on 16 distinct 16-byte bank groups;
+        //        V: the 4 rows one transposing read touches land on 4 distinct 64-byte quarters.
+        //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
+        //      based at the tile and bounded by the slice, so keys past sk land as zeros.
+        auto kswz = [](int r) __attribute__((always_inline)) {
+            return KROWB % 256 == 0 ? (r & 15) : ((r >> 1) & 7);    // rows of 256 B, else 128/384 B
+        };
+        auto vswz = [](int r) __attribute__((always_inline)) {
+            return VROWB % 256 == 0 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+        };
+        uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int i = 0; i < KDMA; ++i) {
+            const int pos = (wave * KDMA + i) * 1024 + lane * 16;
+            const int r = pos / KROWB, pc = (pos % KROWB) / 16;
+            kgo[i] = static_cast<uint32_t>(r * p.kv.ss * 2 + ((pc ^ kswz(r)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < VDMA; ++i) {
+            const int pos = (wave * VDMA + i) * 1024 + lane * 16;
+            const int r = pos / VROWB, pc = (pos % VROWB) / 16;
+            vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
+        }
+        auto tile_rsrc = [&](const char* base, const View& vw, uint32_t slice, int t) __attribute__((always_inline)) {
+            const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
+            const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
+            return make_rsrc(left ? base + start : base, left);
+        };
+        // past the last tile the buffer range is empty: nothing is read
+        auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+            const auto r = tile_rsrc(kbase, p.kv, kslice, t);
+#pragma unroll
+            for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
+        };
+        auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
+            const auto r = tile_rsrc(vbase, p.vv, vslice, t);
+#pragma unroll
+            for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
+        };
+
+        // LDS starts as zeros so that any row the DMA does not fill holds finite values
+        if (!lds_zeroed) {
+            lds_zeroed = true;
+            for (int i = tid; i < KTILE / 16; i += NTHREADS) {
+                reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
+                reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
+            }
+            for (int i = tid; i < VTILE / 16; i += NTHREADS) {
+                reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
+                reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
+            }
+            __syncthreads();
+        }
+
+        f32x16 oacc[CBLK];
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
+        float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
+        float l_run = 0.f;       // this lane's partial row sum over its half of the keys
+
+        // fragment addresses inside a slot (bytes)
+        const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
+        const int t16 = lane & 15;
+        // V transposing reads: lane t of a 16-lane group points at key (k0 + t/4), channel
+        // (c0 + 4*(t%4)); the group then receives, lane by lane, 16 consecutive channels of 4 keys.
+        const int vkey_l = half * 4 + (t16 >> 2);                 // key offset inside a 16-key step
+        const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3); // channel offset inside a 32-block
+
+        // K fragment of k-step kk: row (kb*32 + col), 16-byte chunk (2*kk + half) ^ kx.  The swizzle
+        // only permutes chunks inside aligned groups of KSW chunks, so the address is one of
+        // KSW/2 per-lane offsets plus an immediate.
+        constexpr int KSW = KROWB % 256 == 0 ? 16 : 8;
+        uint32_t koff[KSW / 2];
+#pragma unroll
+        for (int j = 0; j < KSW / 2; ++j) koff[j] = col * KROWB + ((2 * j + half) ^ kx) * 16;
+
+        // ---- S^T = K Q^T for the 32-key block kb of a K tile (one accumulator)
+        auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
+            s = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const uint8_t* a_ptr = kl + koff[kk % (KSW / 2)] + (kk / (KSW / 2)) * KSW * 16 + kb * 32 * KROWB;
+                const auto a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_ptr));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+            }
+        };
+        // ---- scores of keys past sk, or above the diagonal, become -inf (block u = keys 32u ..)
+        auto need_mask = [&](int u) __attribute__((always_inline)) {
+            const int key0 = u * 32;
+            return (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
+        };
+        auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (key >= sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
+            }
+        };
+        // ---- this lane's max over its 16 scores of a block
+        auto lane_max = [&](const f32x16& s) __attribute__((always_inline)) {
+            float a = __builtin_fmaxf(s[0], s[1]);
+            float b = __builtin_fmaxf(s[14], s[15]);
+#pragma unroll
+            for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
+#pragma unroll
+            for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
+            return __builtin_fmaxf(a, b);
+        };
+        // ---- online softmax update from a block max (the reference max only moves when a row's
+        //      max grows by more than 2^8 in probability); returns m * c for the exponentials
+        auto softmax_update = [&](float mx) __attribute__((always_inline)) {
+            const float mt = fmaxf(mx, swap_halves(mx));
+            const float m_new = fmaxf(m_run, mt);
+            const bool grow = m_new > m_run && (m_run == kNegInf || (m_new - m_run) * c > kRescaleThreshold);
+            if (__any(grow)) {
+                const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
+                l_run *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+                m_run = m_new;
+            }
+            return m_run == kNegInf ? 0.f : m_run * c;
+        };
+        // ---- P^T = exp2(S^T c - m c) rounded to bf16, as the B operands of two 16-key P.V steps
+        auto exp_block = [&](const f32x16& s, float mc, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, -mc));
+                    const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, -mc));
+                    w[i] = pack_bf16x2(p0, p1);
+                }
+                pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        };
+        // ---- row sum of the rounded P fed to P.V
+        auto row_sum = [&](const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+            float a = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+            }
+            l_run += a;
+        };
+        // ---- O^T += V^T P^T over the 32-key block kb of a V tile: the A operand (32 channels x
+        //      16 keys) comes from two transposing reads of row-major V; keys ks*16 +
+        //      {half*4 .. +3} and {8 + half*4 .. +3} match the key order of P^T's B operand
+        auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int cb = 0; cb < CBLK; ++cb) {
+                    u32x2 part[2];
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int key = kb * 32 + ks * 16 + r * 8 + vkey_l;
+                        const int ch = cb * 32 + vch_l;
+                        const int chunk = (ch >> 3) ^ vswz(key);
+                        part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
+                    }
+                    const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
+                }
+            }
+        };
+
+        // Instruction counts of the interleaved regions (per wave and 32-key block).
+        constexpr int EXP_VALU = 16 + 16 + 8;           // FMA + exp per score, one pack per pair
+        constexpr int PV_MFMA = 2 * CBLK;               // two transposing V reads per MFMA
+        constexpr int PV_VALU = 8 + 8 + 1;              // row-sum dot2 + next block's max chain
+        constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
+        constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
+        constexpr int WAIT_K0 = (VM_PROLOGUE & 15) | ((VM_PROLOGUE >> 4) << 14) | 0x0F70;
+        static_assert(VM_PROLOGUE < 64, "vmcnt is 6 bits");
+        // region A: S of the next block (KSTEPS MFMAs, one K read each) under the exponentials
+        //           of the current block
+        auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float mc,
+                            bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_barrier(0);
+            qk_block(kl, kb, sn);
+            exp_block(s, mc, pf);
+            // keep the exponentials here: without a use inside the region the compiler would sink
+            // them to the P.V MFMAs that consume them
+            asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+            sched_region<KSTEPS, KSTEPS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // region B: P.V of the current block under its row sum and the next block's lane max
+        auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], const f32x16& sn,
+                            auto vmem_c) __attribute__((always_inline)) {
+            pv_block(vl, kb, pf);
+            row_sum(pf);
+            const float mx = lane_max(sn);
+            sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+                std::make_integer_sequence<int, PV_MFMA>{});
+            __builtin_amdgcn_sched_barrier(0);
+            return mx;
+        };
+
+        // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks: block
+        //      u's exponentials run under the S MFMAs of block u+1, and block u's P.V under the
+        //      lane max of block u+1.  Tile t's K sits in k slot t%2 and its V in v slot t%2.
+        //      The barrier of iteration t (after the S MFMAs of its second block) guarantees
+        //      that every wave's part of V_t and K_{t+1} has landed and that no wave still reads
+        //      K_t or V_{t-1}: their slots then take K_{t+2} and V_{t+1}.
+        using NoVmem = std::integral_constant<int, 0>;
+        using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
+        // a tile that is not the last: its two blocks and the S of the next tile's first block
+        auto iteration = [&](int t, auto par_c, f32x16& s, float& mx) __attribute__((always_inline)) {
+            using Cur = std::integral_constant<int, decltype(par_c)::value>;
+            using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+            f32x16 sn;
+            bf16x8 pf[2];
+            // block 2t (exponentials, P.V) with block 2t+1 (S, max)
+            float mc = softmax_update(mx);
+            region_a(k_slot(Cur{}), 1, sn, s, mc, pf);
+            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+            __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_k(t + 2, k_slot(Cur{}));
+            issue_v(t + 1, v_slot(Nxt{}));
+            mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{});
+            s = sn;
+            // block 2t+1 with block 2t+2 (the first block of the next tile)
+            mc = softmax_update(mx);
+            region_a(k_slot(Nxt{}), 0, sn, s, mc, pf);
+            if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
+            __builtin_amdgcn_sched_barrier(0);
+            mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{});
+            s = sn;
+        };
+        // the last tile: its two blocks, nothing further to load
+        auto last = [&](int t, auto par_c, const f32x16& s0, float mx) __attribute__((always_inline)) {
+            using Cur = std::integral_constant<int, decltype(par_c)::value>;
+            f32x16 sn;
+            bf16x8 pf[2];
+            float mc = softmax_update(mx);
+            region_a(k_slot(Cur{}), 1, sn, s0, mc, pf);
+            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+            __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{});
+            mc = softmax_update(mx);
+            exp_block(sn, mc, pf);
+            row_sum(pf);
+            pv_block(v_slot(Cur{}), 1, pf);
+        };
+
+        if (ntiles > 0) {
+            using Zero = std::integral_constant<int, 0>;
+            using One = std::integral_constant<int, 1>;
+            issue_k(0, k_slot(Zero{}));
+            issue_v(0, v_slot(Zero{}));
+            issue_k(1, k_slot(One{}));
+            __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
+            __syncthreads();
+            f32x16 s;
+            qk_block(k_slot(Zero{}), 0, s);
+            if (need_mask(0)) mask_block(0, s);
+            float mx = lane_max(s);
+            int t = 0;
+            for (; t + 2 < ntiles; t += 2) {
+                iteration(t, Zero{}, s, mx);
+                iteration(t + 1, One{}, s, mx);
+            }
+            if (t + 1 < ntiles) {
+                iteration(t, Zero{}, s, mx);
+                last(t + 1, One{}, s, mx);
+            } else {
+                last(t, Zero{}, s, mx);
+            }
+        }
+
+        // ---- epilogue: normalise, store O (bf16) and LSE
+        const float l_tot = l_run + swap_halves(l_run);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (my_row < sq) {
+            uint16_t* orow = static_cast<uint16_t*>(p.o) + (orow0 + h * p.ov.sh + my_row * p.ov.ss);
 #pragma unroll
             for (int cb = 0; cb < CBLK; ++cb) {
-                u32x2 part[2];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int key = kb * 32 + ks * 16 + r * 8 + vkey_l;
-                    const int ch = cb * 32 + vch_l;
-                    const int chunk = (ch >> 3) ^ vswz(key);
-                    part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int ch = cb * 32 + grp * 8 + half * 4;
+                    const uint32_t w0 = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
+                    const uint32_t w1 = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + ch) = u32x2{w0, w1};
                 }
-                const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
             }
-        }
-    };
-
-    // Instruction counts of the interleaved regions (per wave and 32-key block).
-    constexpr int EXP_VALU = 16 + 16 + 8;           // FMA + exp per score, one pack per pair
-    constexpr int PV_MFMA = 2 * CBLK;               // two transposing V reads per MFMA
-    constexpr int PV_VALU = 8 + 8 + 1;              // row-sum dot2 + next block's max chain
-    constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
-    constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
-    constexpr int WAIT_K0 = (VM_PROLOGUE & 15) | ((VM_PROLOGUE >> 4) << 14) | 0x0F70;
-    static_assert(VM_PROLOGUE < 64, "vmcnt is 6 bits");
-    // region A: S of the next block (KSTEPS MFMAs, one K read each) under the exponentials
-    //           of the current block
-    auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float mc,
-                        bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block(kl, kb, sn);
-        exp_block(s, mc, pf);
-        // keep the exponentials here: without a use inside the region the compiler would sink
-        // them to the P.V MFMAs that consume them
-        asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-        sched_region<KSTEPS, KSTEPS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // region B: P.V of the current block under its row sum and the next block's lane max
-    auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], const f32x16& sn,
-                        auto vmem_c) __attribute__((always_inline)) {
-        pv_block(vl, kb, pf);
-        row_sum(pf);
-        const float mx = lane_max(sn);
-        sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
-            std::make_integer_sequence<int, PV_MFMA>{});
-        __builtin_amdgcn_sched_barrier(0);
-        return mx;
-    };
-
-    // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks: block
-    //      u's exponentials run under the S MFMAs of block u+1, and block u's P.V under the
-    //      lane max of block u+1.  Tile t's K sits in k slot t%2 and its V in v slot t%2.
-    //      The barrier of iteration t (after the S MFMAs of its second block) guarantees
-    //      that every wave's part of V_t and K_{t+1} has landed and that no wave still reads
-    //      K_t or V_{t-1}: their slots then take K_{t+2} and V_{t+1}.
-    using NoVmem = std::integral_constant<int, 0>;
-    using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
-    // a tile that is not the last: its two blocks and the S of the next tile's first block
-    auto iteration = [&](int t, auto par_c, f32x16& s, float& mx) __attribute__((always_inline)) {
-        using Cur = std::integral_constant<int, decltype(par_c)::value>;
-        using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
-        f32x16 sn;
-        bf16x8 pf[2];
-        // block 2t (exponentials, P.V) with block 2t+1 (S, max)
-        float mc = softmax_update(mx);
-        region_a(k_slot(Cur{}), 1, sn, s, mc, pf);
-        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_k(t + 2, k_slot(Cur{}));
-        issue_v(t + 1, v_slot(Nxt{}));
-        mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{});
-        s = sn;
-        // block 2t+1 with block 2t+2 (the first block of the next tile)
-        mc = softmax_update(mx);
-        region_a(k_slot(Nxt{}), 0, sn, s, mc, pf);
-        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
-        __builtin_amdgcn_sched_barrier(0);
-        mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{});
-        s = sn;
-    };
-    // the last tile: its two blocks, nothing further to load
-    auto last = [&](int t, auto par_c, const f32x16& s0, float mx) __attribute__((always_inline)) {
-        using Cur = std::integral_constant<int, decltype(par_c)::value>;
-        f32x16 sn;
-        bf16x8 pf[2];
-        float mc = softmax_update(mx);
-        region_a(k_slot(Cur{}), 1, sn, s0, mc, pf);
-        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{});
-        mc = softmax_update(mx);
-        exp_block(sn, mc, pf);
-        row_sum(pf);
-        pv_block(v_slot(Cur{}), 1, pf);
-    };
-
-    if (ntiles > 0) {
-        using Zero = std::integral_constant<int, 0>;
-        using One = std::integral_constant<int, 1>;
-        issue_k(0, k_slot(Zero{}));
-        issue_v(0, v_slot(Zero{}));
-        issue_k(1, k_slot(One{}));
-        __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
-        __syncthreads();
-        f32x16 s;
-        qk_block(k_slot(Zero{}), 0, s);
-        if (need_mask(0)) mask_block(0, s);
-        float mx = lane_max(s);
-        int t = 0;
-        for (; t + 2 < ntiles; t += 2) {
-            iteration(t, Zero{}, s, mx);
-            iteration(t + 1, One{}, s, mx);
-        }
-        if (t + 1 < ntiles) {
-            iteration(t, Zero{}, s, mx);
-            last(t + 1, One{}, s, mx);
-        } else {
-            last(t, Zero{}, s, mx);
+            if (p.lse != nullptr && half == 0) {
+                const float lse = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
+                p.lse[lse0 + my_row] = lse;
+            }
         }
     }
-
-    // ---- epilogue: normalise, store O (bf16) and LSE
-    const float l_tot = l_run + swap_halves(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_row < sq) {
-        uint16_t* orow = static_cast<uint16_t*>(p.o) + (orow0 + h * p.ov.sh + my_row * p.ov.ss);
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int ch = cb * 32 + grp * 8 + half * 4;
-                const uint32_t w0 = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
-                const uint32_t w1 = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + ch) = u32x2{w0, w1};
-            }
-        }
-        if (p.lse != nullptr && half == 0) {
-            const float lse = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
-            p.lse[lse0 + my_row] = lse;
+item_done: __attribute__((unused));
+    if constexpr (PAIRED) {
+        // the pair's light block: the slots are rewritten only after every wave is done
+        if (mblk != mrev) {
+            mblk = mrev;
+            __syncthreads();
+            goto next_item;
         }
     }
 }
@@ -496,11 +524,28 @@ template <int DQK, int DV, bool CAUSAL, bool VARLEN>
 hipError_t launch(AttnParams p, hipStream_t stream) {
     constexpr int BM = TileCfg<DQK, DV>::BM;
     p.n_mblocks = (p.sq + BM - 1) / BM;
-    const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
-    if (nwg == 0) return hipSuccess;
+    const int64_t blocks = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
+    if (blocks == 0) return hipSuccess;
+    // Pair causal query blocks when the grid fills the device a few times at most; on longer
+    // grids the hardware's dispatch already overlaps short and long workgroups (measured:
+    // pairing gains 5-10% on 2-8 rounds, nothing on 16).
+    bool paired = false;
+    if (CAUSAL && p.n_mblocks > 1) {
+        int groups = 0;
+        const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL>;
+        const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2, &groups);
+        if (e != hipSuccess) return e;
+        paired = blocks <= 8 * static_cast<int64_t>(groups);
+    }
+    const int64_t nwg = paired ? static_cast<int64_t>(p.b) * p.hq * ((p.n_mblocks + 1) / 2) : blocks;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(BM * 2), 0, stream, p);
+    if (paired) {
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL>), dim3(static_cast<unsigned>(nwg)),
+                           dim3(BM * 2), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false>), dim3(static_cast<unsigned>(nwg)),
+                           dim3(BM * 2), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@ struct AttnParams {
     int total_q = 0, total_k = 0;
 };
 
+// Workgroups of `kernel` (launched with `threads` threads, no dynamic LDS) that the current
+// device holds at once: CUs x resident workgroups per CU.  Cached per device and kernel.
+hipError_t resident_groups(const void* kernel, int threads, int* groups);
+
 // bf16 attention forward: d_qk/d_v in {(64,64), (128,128), (192,128)}.
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream);
 

@@ -16,7 +16,10 @@ Sources (web pages; cited by title and section):
     PR 7754): the per-head K mean and its gate (Summary, PR-specific
     question, commit message).
   * "MHA v4: fixes, refactor, new kernel, perf tweaks" (ROCm aiter PR 5335):
-    the BF16/FP8 recipe of mha_v4 (Motivation, Kernels list).
+    the BF16/FP8 recipe of mha_v4 (Motivation, Kernels list) and its MX
+    descales (review comments).
+  * OCP Microscaling Formats (MX) v1.0: the MXFP8 block format that the pages
+    name but do not define.
 
 Modules:
   attention  - softmax(scale * Q K^T + causal mask) V with GQA, and the
@@ -26,6 +29,8 @@ Modules:
                gate decision, mean output (the algorithm's steps).
   fp8        - OCP E4M3 rounding, per-128-token-block scaling, and attention
                on the dequantised, smoothed tensors (the algorithm's steps).
+  mx         - MXFP8: E4M3 elements with one E8M0 exponent per 32 channels,
+               and attention on the dequantised, smoothed tensors.
 
 Every function is pinned by a ``-m "not gpu"`` test against facts fixed
 outside this package: closed forms, hand-derived examples under
@@ -43,3 +48,4 @@ from .fp8 import (  # noqa: F401
     quantize_blocks,
     fp8_attention_forward,
 )
+from .mx import mx_quantize, mx_dequantize, mxfp8_attention_forward  # noqa: F401

@@ -174,3 +174,71 @@ def test_fp8_source_passes_pins():
 @pytest.mark.parametrize("name,old,new", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
 def test_fp8_mutant_is_caught(name, old, new):
     assert not _fp8_pins_pass(_load("fp8.py", old, new, extra=_fp8_extra()))
+
+
+# ---------------------------------------------------------------- MXFP8 pins
+
+def _mx_pins_pass(mod):
+    try:
+        for c in _golden("mx_worked_examples.json")["cases"]:
+            x = np.zeros(32, dtype=np.float32)
+            x[: len(c["x"])] = np.asarray(c["x"], dtype=np.float32)
+            codes, exps, values = mod.mx_quantize(x)
+            n = len(c["codes"])
+            if exps.shape != (1,) or int(exps[0]) != c["exp_byte"]:
+                return False
+            if [int(v) for v in codes[:n]] != [int(v, 16) for v in c["codes"]] or list(values[:n]) != c["values"]:
+                return False
+        x = (RNG.standard_normal((4, 64)) * 3).astype(np.float32)
+        c0, e0, _ = mod.mx_quantize(x)
+        c1, e1, _ = mod.mx_quantize((x * np.float32(8.0)).astype(np.float32))
+        if not (np.array_equal(c0, c1) and np.array_equal(e1.astype(int), e0.astype(int) + 3)):
+            return False
+        y = np.abs(x.astype(np.float64)).reshape(4, 2, 32).max(axis=2) / np.ldexp(1.0, e0.astype(int) - 127)
+        if not np.all((y >= 256) & (y < 512)):
+            return False
+    except Exception:
+        return False
+    return True
+
+
+def _mx_extra():
+    from oracle.attention import attention_forward
+    from oracle.fp8 import e4m3_decode, e4m3_encode, e4m3_round, smooth_k
+    return {"attention_forward": attention_forward, "e4m3_decode": e4m3_decode, "e4m3_encode": e4m3_encode,
+            "e4m3_round": e4m3_round, "smooth_k": smooth_k}
+
+
+MX_ANCHOR = "from .fp8 import e4m3_decode, e4m3_encode, e4m3_round, smooth_k"
+
+MX_MUTANTS = [
+    ("emax_7", "E4M3_EMAX = 8", "E4M3_EMAX = 7"),
+    ("ceil_log2", "shared = (e2.astype(np.int64) - 1) - E4M3_EMAX", "shared = e2.astype(np.int64) - E4M3_EMAX"),
+    ("bias_128", "E8M0_BIAS = 127", "E8M0_BIAS = 128"),
+    ("block_16", "MX_BLOCK = 32", "MX_BLOCK = 16"),
+    ("zero_block_byte", "exps = np.where(amax > 0, shared + E8M0_BIAS, 0).astype(np.uint8)",
+     "exps = (shared + E8M0_BIAS).astype(np.uint8)"),
+    ("scale_multiplied", "q = e4m3_round(blocks / scale)", "q = e4m3_round(blocks * scale)"),
+]
+
+
+def _load_mx(old=None, new=None):
+    path = os.path.join(ROOT, "oracle", "mx.py")
+    src = open(path).read().replace(MX_ANCHOR, "")
+    if old is not None:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new, 1)
+    src = src.replace("from .attention import attention_forward", "")
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__.update(_mx_extra())
+    exec(compile(src, path, "exec"), mod.__dict__)
+    return mod
+
+
+def test_mx_source_passes_pins():
+    assert _mx_pins_pass(_load_mx())
+
+
+@pytest.mark.parametrize("name,old,new", MX_MUTANTS, ids=[m[0] for m in MX_MUTANTS])
+def test_mx_mutant_is_caught(name, old, new):
+    assert not _mx_pins_pass(_load_mx(old, new))

@@ -7,8 +7,9 @@ One step = one mha_fwd_bf16 call on the headline workload (b1 hq128 hk128
 8192^2 dqk192/dv128 causal, bf16), inputs resident in HBM.  The timed region is
 exactly K steps bracketed by torch.cuda.synchronize(); the kernel's average
 duration comes from HIP events recorded on the stream the kernel runs on.
-The same run also times the quantised path on its own workload (b1 h16 4096^2
-d128 non-causal: k_smooth_mean + mha_fwd_fp8) and reports it under "fp8_call".
+The same run also times the quantised path on its own workloads (b1 h16 4096^2
+d128 non-causal: k_smooth_mean + mha_fwd_fp8, and the same with mha_fwd_mxfp8)
+and reports them under "fp8_call" and "mxfp8_call".
 
 Prints ONE JSON line.  Extra modes used for HBM-traffic calibration:
     python bench.py --calibrate-copy BYTES   (a plain device copy of BYTES, for counter scaling)
@@ -33,7 +34,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # the bf16 shapes, the gate page's eager mha_v4 call (MI355X) for the FP8 ones.
 PAGES_BF16_US = {"mla_d192_d128_causal": 4083.2, "mla_d192_d128_noncausal": 7086.1,
                  "gqa_d128_8192_causal": 2686.6, "gqa_d64_causal": 333.0}
-PAGES_FP8_CALL_US = {"fp8_ksmooth_d128": 219.2, "fp8_long_h5": 3857.2}
+PAGES_FP8_CALL_US = {"fp8_ksmooth_d128": 219.2, "fp8_long_h5": 3857.2, "mxfp8_ksmooth_d128": 140.8}
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_mla_d192_d128_causal_traffic.json")
 KERNEL_SOURCES = ["head_attention_forward_flash_amd/csrc/attn_fwd_bf16.hip",
@@ -117,32 +118,35 @@ def cpu_baseline(w, q, k, v, budget_s=12.0, max_heads=64):
 
 
 def bench_fp8(steps, warmup, dev, name="fp8_ksmooth_d128"):
-    """k_smooth_mean + mha_fwd_fp8 on an FP8 workload; None when the fp8 kernel is not built."""
+    """k_smooth_mean + the quantised call (mha_fwd_fp8, or mha_fwd_mxfp8 for an MXFP8 workload)."""
     import torch
     import head_attention_forward_flash_amd as mha
     import workloads
     w = workloads.WORKLOADS[name]
     q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
     o = torch.empty((w.b, w.sq, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(mha.mha_fwd_fp8_workspace_bytes(w.b, w.hq, w.hk, w.sq, w.sk, w.d_qk), dtype=torch.uint8,
-                     device=dev)
+    fwd = mha.mha_fwd_mxfp8 if w.mx else mha.mha_fwd_fp8
+    ws_bytes = (mha.mha_fwd_mxfp8_workspace_bytes if w.mx else mha.mha_fwd_fp8_workspace_bytes)(
+        w.b, w.hq, w.hk, w.sq, w.sk, w.d_qk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     gws = torch.empty(max(256, mha.k_smooth_mean_workspace_bytes(w.b, w.hk, w.sk, w.d_qk)), dtype=torch.uint8,
                       device=dev)
     try:
         mean, _ = mha.k_smooth_mean(k, workspace=gws)
-        mha.mha_fwd_fp8(q, k, v, k_mean=mean, out=o, workspace=ws, lse=False)
+        fwd(q, k, v, k_mean=mean, out=o, workspace=ws, lse=False)
     except mha.MhaError as e:
         return {"available": False, "reason": str(e)}
     stream = torch.cuda.current_stream(dev)
 
     def call():
         m, _ = mha.k_smooth_mean(k, workspace=gws)
-        mha.mha_fwd_fp8(q, k, v, k_mean=m, out=o, workspace=ws, lse=False)
+        fwd(q, k, v, k_mean=m, out=o, workspace=ws, lse=False)
 
     ms, _ = time_launches(call, steps, warmup, stream)
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"available": True, "workload": w.name, "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 1),
             "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "pages_us_per_call": PAGES_FP8_CALL_US.get(w.name),
+            "recipe": "mxfp8 (E8M0 per 32 channels)" if w.mx else "fp8 (fp32 scale per 128 tokens)",
             "includes": "k_smooth_mean (2 kernels) + quantisation + fp8 attention, device time by HIP events"}
 
 
@@ -235,6 +239,7 @@ def main():
                 "traffic": None if traffic is None else int(traffic)}
 
     fp8 = None if a.no_fp8 else bench_fp8(max(20, a.steps), a.warmup, dev, a.fp8_workload)
+    mxfp8 = None if a.no_fp8 else bench_fp8(max(20, a.steps), a.warmup, dev, "mxfp8_ksmooth_d128")
     cpu = None if a.no_cpu_baseline else cpu_baseline(w, qc, kc, vc)
 
     pages_tflops = w.flops() / (PAGES_BF16_US[w.name] * 1e-6) / 1e12 if w.name in PAGES_BF16_US else None
@@ -259,6 +264,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fp8_call": fp8,
+        "mxfp8_call": mxfp8,
     }
     print(json.dumps(out), flush=True)
 

@@ -32,7 +32,8 @@ STATUS_NAMES = {
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = (
     "mha_fwd_bf16", "mha_fwd_bf16_varlen", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
-    "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_status_string", "mha_last_error",
+    "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
+    "mha_fwd_mxfp8", "mha_status_string", "mha_last_error",
 )
 
 
@@ -76,6 +77,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_fwd_fp8.restype = i32
     lib.mha_fwd_fp8.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, vp, Strides, vp,
                                 i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mha_fwd_mxfp8_workspace_bytes.restype = sz
+    lib.mha_fwd_mxfp8_workspace_bytes.argtypes = [i32] * 6
+    lib.mha_mxfp8_workspace_layout.restype = i32
+    lib.mha_mxfp8_workspace_layout.argtypes = [i32] * 6 + [ctypes.POINTER(sz)]
+    lib.mha_fwd_mxfp8.restype = i32
+    lib.mha_fwd_mxfp8.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, vp, Strides, vp,
+                                  i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_status_string.argtypes = [i32]
     lib.mha_last_error.restype = ctypes.c_char_p
@@ -216,11 +224,8 @@ def mha_fp8_workspace_layout(b, hq, hk, sq, sk, d):
     return [int(x) for x in arr]
 
 
-def mha_fwd_fp8(q, k, v, k_mean=None, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
-                lse: bool = True, workspace=None):
-    """K-smoothed FP8 attention forward. Returns (o, lse, workspace)."""
+def _fwd_quantised(entry, need_fn, q, k, v, k_mean, causal, softmax_scale, out, lse, workspace):
     torch = _torch()
-    lib = load_library()
     _require_device(q, k, v, k_mean, out)
     b, sq, hq, d = q.shape
     _, sk, hk, _ = k.shape
@@ -229,13 +234,38 @@ def mha_fwd_fp8(q, k, v, k_mean=None, causal: bool = False, softmax_scale: Optio
     if out is None:
         out = torch.empty((b, sq, hq, d), dtype=torch.bfloat16, device=q.device)
     lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
-    need = mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d)
+    need = need_fn(b, hq, hk, sq, sk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if k_mean is not None and (k_mean.dtype != torch.float32 or not k_mean.is_contiguous()):
         raise ValueError("k_mean must be a contiguous float32 [b, hk, d] tensor")
-    _check(lib.mha_fwd_fp8(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
-                           _ptr(k_mean), _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d,
-                           float(softmax_scale), int(bool(causal)), _ptr(workspace), workspace.numel(),
-                           _stream(q.device)))
+    _check(entry(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
+                 _ptr(k_mean), _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d,
+                 float(softmax_scale), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out, lse_t, workspace
+
+
+def mha_fwd_fp8(q, k, v, k_mean=None, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
+                lse: bool = True, workspace=None):
+    """K-smoothed FP8 attention forward. Returns (o, lse, workspace)."""
+    return _fwd_quantised(load_library().mha_fwd_fp8, mha_fwd_fp8_workspace_bytes, q, k, v, k_mean, causal,
+                          softmax_scale, out, lse, workspace)
+
+
+def mha_fwd_mxfp8_workspace_bytes(b, hq, hk, sq, sk, d) -> int:
+    return int(load_library().mha_fwd_mxfp8_workspace_bytes(b, hq, hk, sq, sk, d))
+
+
+def mha_mxfp8_workspace_layout(b, hq, hk, sq, sk, d):
+    """Byte offsets of (q codes, k codes, v values as bf16, q exponents, k exponents) in the MXFP8 workspace."""
+    lib = load_library()
+    arr = (ctypes.c_size_t * 5)()
+    _check(lib.mha_mxfp8_workspace_layout(b, hq, hk, sq, sk, d, arr))
+    return [int(x) for x in arr]
+
+
+def mha_fwd_mxfp8(q, k, v, k_mean=None, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
+                  lse: bool = True, workspace=None):
+    """K-smoothed MXFP8 attention forward (E8M0 exponent per 32 channels). Returns (o, lse, workspace)."""
+    return _fwd_quantised(load_library().mha_fwd_mxfp8, mha_fwd_mxfp8_workspace_bytes, q, k, v, k_mean, causal,
+                          softmax_scale, out, lse, workspace)

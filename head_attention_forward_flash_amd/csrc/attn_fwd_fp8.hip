@@ -25,6 +25,16 @@
 //                  V scale of its block.
 // Masked scores are -inf; the per-tile factor is at least FLT_MIN, so they reach
 // the exponential as -inf and come out as exactly 0.
+//
+// MXFP8 (MX = true): Q and K codes carry one E8M0 exponent per 32 channels of a
+// row instead of block scales, which go in as the scaled MFMA's per-lane scale
+// operands, so S comes out fully scaled.  The instruction applies the scale of
+// lane r (r < 32) to the first 16 bytes of lanes r AND r + 32, and that of lane
+// r + 32 to their last 16 bytes (measured), so in a 64-channel k-step lane half
+// h holds channels [16h, 16h + 16) and [32 + 16h, 32 + 16h + 16): the first 32
+// channels then get lane r's scale, the next 32 lane r + 32's.  V arrives with
+// its exponents applied, so the per-tile factor is the softmax scale alone and
+// P carries no V scale.
 
 #include <type_traits>
 #include <utility>
@@ -64,7 +74,7 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool MX>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
     constexpr int NWAVES = NTHREADS / 64;
     constexpr int KROWB = D;                  // bytes per K8 row
@@ -116,9 +126,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const auto qrs = make_rsrc(p.q + static_cast<int64_t>(bh) * qslice, qslice);
     const uint8_t* kbase = p.k + static_cast<int64_t>(bg) * kslice;
     const uint8_t* vbase = p.v + static_cast<int64_t>(bg) * vslice;
-    const float q_scale = p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
-    const float* k_scale = p.k_scale + static_cast<int64_t>(bg) * p.nk;
-    const float* v_scale = p.v_scale + static_cast<int64_t>(bg) * p.nk;
+    const float q_scale = MX ? 1.f : p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
+    const float* k_scale = MX ? nullptr : p.k_scale + static_cast<int64_t>(bg) * p.nk;
+    const float* v_scale = MX ? nullptr : p.v_scale + static_cast<int64_t>(bg) * p.nk;
+    // MXFP8 exponents: 4 bytes per row (one per 32 channels), rows padded like the codes
+    const uint32_t exp_slice = static_cast<uint32_t>(p.nk) * BM * 4;
+    const auto kers = make_rsrc(MX ? p.k_exps + static_cast<int64_t>(bg) * exp_slice : nullptr, MX ? exp_slice : 0u);
 
     const int wave_row0 = mblk * BM + wave * 32;
     const int my_row = wave_row0 + col;
@@ -129,12 +142,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     i32x8 qf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t off = static_cast<uint32_t>(my_row * D + ks * 64 + half * 32);
+        // plain fp8: channels [32h, 32h + 32) of the k-step; MXFP8: [16h, +16) and [32 + 16h, +16)
+        const uint32_t off = static_cast<uint32_t>(my_row * D + ks * 64 + half * (MX ? 16 : 32));
         const u32x4 a = buffer_load_b128(qrs, off) ^ qsign;
-        const u32x4 b = buffer_load_b128(qrs, off + 16) ^ qsign;
+        const u32x4 b = buffer_load_b128(qrs, off + (MX ? 32 : 16)) ^ qsign;
         qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
     const float cq = q_scale * fabsf(p.scale_log2);   // base-2 factor of this block's scores, >= 0
+    // MXFP8: the E8M0 byte of each k-step's 32 channels of this lane's query, in bits 0-7
+    uint32_t qe[2] = {0u, 0u};
+    if constexpr (MX) {
+        const uint32_t qslice_e = static_cast<uint32_t>(p.nq) * BM * 4;
+        const auto qers = make_rsrc(p.q_exps + static_cast<int64_t>(bh) * qslice_e, qslice_e);
+        const uint32_t w = buffer_load_b32(qers, static_cast<uint32_t>(my_row * 4));
+        qe[0] = w >> (8 * half);
+        qe[1] = w >> (8 * (2 + half));
+    }
+    // MXFP8: the exponent words of this lane's key in the two 32-key blocks of tile t (zeros
+    // past the padded key range)
+    auto kexp_load = [&](int t) __attribute__((always_inline)) {
+        const uint32_t key = static_cast<uint32_t>(t * BN + col);
+        return u32x2{buffer_load_b32(kers, key * 4), buffer_load_b32(kers, (key + 32) * 4)};
+    };
 
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
     const int ntiles = (kv_end + BN - 1) / BN;
@@ -144,9 +173,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         float c, log2_sv, inv_sv;
     };
     auto tile_scale = [&](int t) __attribute__((always_inline)) {
-        const int kblk = min((t * BN) / BM, p.nk - 1);   // past the last tile: any valid block
-        const float sv = v_scale[kblk];
-        return TileScale{fmaxf(cq * k_scale[kblk], kMinFactor), __log2f(sv), 1.f / sv};
+        if constexpr (MX) {
+            return TileScale{fmaxf(cq, kMinFactor), 0.f, 1.f};
+        } else {
+            const int kblk = min((t * BN) / BM, p.nk - 1);   // past the last tile: any valid block
+            const float sv = v_scale[kblk];
+            return TileScale{fmaxf(cq * k_scale[kblk], kMinFactor), __log2f(sv), 1.f / sv};
+        }
     };
 
     // ---- DMA layout (see the bf16 kernel): K8 rows of 128 B keep chunk c of row r at
@@ -208,17 +241,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const int vch_l = ((lane >> 4) & 1) * 16 + 4 * (t16 & 3);
 
     // ---- S^T = K8 Q8^T for the 32-key block kb of a K tile
-    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
+    //      (MXFP8: `ke` is the exponent word of this lane's key in block kb)
+    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s, uint32_t ke) __attribute__((always_inline)) {
         const uint8_t* row = kl + (kb * 32 + col) * KROWB;
         s = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int c0 = (ks * 4 + half * 2) ^ kx, c1 = (ks * 4 + half * 2 + 1) ^ kx;
+            // 16-byte chunks of the row in Q's channel order (see the Q fragment)
+            const int c0 = (MX ? ks * 4 + half : ks * 4 + half * 2) ^ kx;
+            const int c1 = (MX ? ks * 4 + half + 2 : ks * 4 + half * 2 + 1) ^ kx;
             const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + c0 * 16);
             const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + c1 * 16);
             const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s, 0, 0, 0, 0, 0, 0);
+            if constexpr (MX) {
+                // E8M0 of channel block 2ks + half in byte 0: lane half 0 scales the k-step's
+                // first 32 channels, lane half 1 the next 32
+                const uint32_t sk = ke >> (8 * (2 * ks + half));
+                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s, 0, 0, 0, static_cast<int>(sk), 0,
+                                                                    static_cast<int>(qe[ks]));
+            } else {
+                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s, 0, 0, 0, 0, 0, 0);
+            }
         }
     };
     auto need_mask = [&](int u) __attribute__((always_inline)) {
@@ -312,10 +356,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     constexpr int WAIT_K0 = VM_PROLOGUE | 0x0F70;
     // region A: S of the next block (2 fp8 MFMAs, 4 K reads) under the exponentials of the
     //           current block
-    auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float c, float bias,
+    auto region_a = [&](const uint8_t* kl, int kb, uint32_t ke, f32x16& sn, const f32x16& s, float c, float bias,
                         bf16x8 (&pf)[2]) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        qk_block(kl, kb, sn);
+        qk_block(kl, kb, sn, ke);
         exp_block(s, c, bias, pf);
         // keep the exponentials here: without a use inside the region the compiler would sink
         // them to the P.V MFMAs that consume them
@@ -340,8 +384,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     //      of iteration t guarantees that every wave's part of V_t and K_{t+1} has landed and
     //      that no wave still reads K_t or V_{t-1}: their slots then take K_{t+2}, V_{t+1}.
     using NoVmem = std::integral_constant<int, 0>;
-    using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
-    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc) __attribute__((always_inline)) {
+    using DmaVmem = std::integral_constant<int, KDMA + VDMA + (MX ? 2 : 0)>;
+    // (MXFP8: ke[0] holds the exponent words of tile t, ke[1] those of tile t+1; the words of
+    // tile t+2 are loaded with its K tile)
+    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc, u32x2 (&ke)[2])
+                         __attribute__((always_inline)) {
         using Cur = std::integral_constant<int, decltype(par_c)::value>;
         using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
         const TileScale sc_next = tile_scale(t + 1);
@@ -349,31 +396,36 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         bf16x8 pf[2];
         // block 2t (exponentials, P.V) with block 2t+1 (S, max)
         float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, sn, s, sc.c, bias, pf);
+        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s, sc.c, bias, pf);
         if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
+        u32x2 ke_new = {0u, 0u};
+        if constexpr (MX) ke_new = kexp_load(t + 2);
         issue_k(t + 2, k_slot(Cur{}));
         issue_v(t + 1, v_slot(Nxt{}));
         mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{});
         s = sn;
         // block 2t+1 with block 2t+2 (the first block of the next tile)
         bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Nxt{}), 0, sn, s, sc.c, bias, pf);
+        region_a(k_slot(Nxt{}), 0, ke[1][0], sn, s, sc.c, bias, pf);
         if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
         __builtin_amdgcn_sched_barrier(0);
         mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, sn, sc_next.c, NoVmem{});
         s = sn;
         sc = sc_next;
+        ke[0] = ke[1];
+        ke[1] = ke_new;
     };
     // the last tile: its two blocks, nothing further to load
-    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc) __attribute__((always_inline)) {
+    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc, const u32x2 (&ke)[2])
+                    __attribute__((always_inline)) {
         using Cur = std::integral_constant<int, decltype(par_c)::value>;
         f32x16 sn;
         bf16x8 pf[2];
         float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, sn, s0, sc.c, bias, pf);
+        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s0, sc.c, bias, pf);
         if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
@@ -388,6 +440,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     if (ntiles > 0) {
         using Zero = std::integral_constant<int, 0>;
         using One = std::integral_constant<int, 1>;
+        u32x2 ke[2] = {{0u, 0u}, {0u, 0u}};
+        if constexpr (MX) {   // issued before the DMA, so the wait below covers them too
+            ke[0] = kexp_load(0);
+            ke[1] = kexp_load(1);
+        }
         issue_k(0, k_slot(Zero{}));
         issue_v(0, v_slot(Zero{}));
         issue_k(1, k_slot(One{}));
@@ -395,19 +452,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         __syncthreads();
         TileScale sc = tile_scale(0);
         f32x16 s;
-        qk_block(k_slot(Zero{}), 0, s);
+        qk_block(k_slot(Zero{}), 0, s, ke[0][0]);
         if (need_mask(0)) mask_block(0, s);
         float mt = row_max(s, sc.c);
         int t = 0;
         for (; t + 2 < ntiles; t += 2) {
-            iteration(t, Zero{}, s, mt, sc);
-            iteration(t + 1, One{}, s, mt, sc);
+            iteration(t, Zero{}, s, mt, sc, ke);
+            iteration(t + 1, One{}, s, mt, sc, ke);
         }
         if (t + 1 < ntiles) {
-            iteration(t, Zero{}, s, mt, sc);
-            last(t + 1, One{}, s, mt, sc);
+            iteration(t, Zero{}, s, mt, sc, ke);
+            last(t + 1, One{}, s, mt, sc, ke);
         } else {
-            last(t, Zero{}, s, mt, sc);
+            last(t, Zero{}, s, mt, sc, ke);
         }
     }
 
@@ -438,12 +495,12 @@ hipError_t launch_attn_fwd_fp8(const Fp8AttnParams& p, int d, bool causal, hipSt
     if (d != D) return hipErrorInvalidValue;
     const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
     if (nwg == 0) return hipSuccess;
-    if (causal)
-        hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), dim3(static_cast<unsigned>(nwg)), dim3(NTHREADS), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_fp8_kernel<false>), dim3(static_cast<unsigned>(nwg)), dim3(NTHREADS), 0,
-                           stream, p);
+    const dim3 grid(static_cast<unsigned>(nwg));
+    const bool mx = p.q_exps != nullptr;
+    if (mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, true>), grid, dim3(NTHREADS), 0, stream, p);
+    if (mx && !causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, true>), grid, dim3(NTHREADS), 0, stream, p);
+    if (!mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, false>), grid, dim3(NTHREADS), 0, stream, p);
+    if (!mx && !causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, false>), grid, dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

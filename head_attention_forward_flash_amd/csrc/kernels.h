@@ -66,6 +66,9 @@ struct QuantParams {
     uint8_t* codes;      // [b, heads, nblk*128, d]: E4M3 codes, or with `widen` their values as bf16
     float* scales;       // [b, heads, nblk]
     bool widen;          // store each code's value widened (exactly) to bf16 instead of the byte
+    bool mx;             // MXFP8: one E8M0 exponent per 32 channels of a token row instead of `scales`;
+                         // widened values then include 2^E
+    uint8_t* exps;       // MXFP8: [b, heads, nblk*128, d/32] E8M0 bytes, or null (not stored)
 };
 
 hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const QuantParams& v,
@@ -78,6 +81,8 @@ struct Fp8AttnParams {
     const float* q_scale;  // [b, hq, nq]
     const float* k_scale;  // [b, hk, nk]
     const float* v_scale;  // [b, hk, nk]
+    const uint8_t* q_exps = nullptr;   // MXFP8 when set: [b, hq, nq*128, 4] E8M0 bytes per 32 channels
+    const uint8_t* k_exps = nullptr;   // [b, hk, nk*128, 4]; V then holds its values with 2^E applied
     void* o;
     View ov;
     float* lse;

@@ -300,13 +300,44 @@ size_t mha_fwd_fp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d)
     return align256(off[5] + size_t(b) * hk * nk * 4);
 }
 
-mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
-                       mha_strides v_stride, const float* k_mean, void* o, mha_strides o_stride, float* lse, int b,
-                       int hq, int hk, int sq, int sk, int d, float softmax_scale, int causal, void* ws,
-                       size_t ws_bytes, void* stream) {
+mha_status mha_mxfp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets) {
+    if (!offsets) return fail(MHA_ERR_NULL, "offsets is NULL");
+    if (b < 0 || hq < 1 || hk < 1 || sq < 0 || sk < 0 || d < 32 || d % 32)
+        return fail(MHA_ERR_SHAPE, "invalid sizes for the mxfp8 workspace");
+    const size_t nq = (size_t(sq) + 127) / 128, nk = (size_t(sk) + 127) / 128;
+    size_t off = 0;
+    offsets[0] = off;
+    off = align256(off + size_t(b) * hq * nq * 128 * d);
+    offsets[1] = off;
+    off = align256(off + size_t(b) * hk * nk * 128 * d);
+    offsets[2] = off;
+    off = align256(off + size_t(b) * hk * nk * 128 * d * 2);   // V values (2^E applied) in bf16
+    offsets[3] = off;
+    off = align256(off + size_t(b) * hq * nq * 128 * (d / 32));
+    offsets[4] = off;
+    return ok();
+}
+
+size_t mha_fwd_mxfp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d) {
+    size_t off[5];
+    if (mha_mxfp8_workspace_layout(b, hq, hk, sq, sk, d, off) != MHA_OK) return 0;
+    const size_t nk = (size_t(sk) + 127) / 128;
+    return align256(off[4] + size_t(b) * hk * nk * 128 * (d / 32));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The quantised call of both recipes: quantiser, then fp8 attention on its output.
+mha_status fwd_quantised(bool mx, const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                         const void* v, mha_strides v_stride, const float* k_mean, void* o, mha_strides o_stride,
+                         float* lse, int b, int hq, int hk, int sq, int sk, int d, float softmax_scale, int causal,
+                         void* ws, size_t ws_bytes, void* stream) {
+    const char* name = mx ? "mxfp8" : "fp8";
     mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
     if (st != MHA_OK) return st;
-    if (d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for fp8; supported: 128", d);
+    if (d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for %s; supported: 128", d, name);
     const bool has_rows = b > 0 && sq > 0;
     if (has_rows && !q) return fail(MHA_ERR_NULL, "q is NULL");
     if (has_rows && sk > 0 && !k) return fail(MHA_ERR_NULL, "k is NULL");
@@ -319,24 +350,28 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     if ((st = make_view("k", k, k_stride, hk, sk, d, 2, true, &kv)) != MHA_OK) return st;
     if ((st = make_view("v", v, v_stride, hk, sk, d, 2, true, &vv)) != MHA_OK) return st;
     if ((st = make_view("o", o, o_stride, hq, sq, d, 2, true, &ov)) != MHA_OK) return st;
-    const size_t need = mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d);
+    const size_t need = mx ? mha_fwd_mxfp8_workspace_bytes(b, hq, hk, sq, sk, d)
+                           : mha_fwd_fp8_workspace_bytes(b, hq, hk, sq, sk, d);
     if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);
     if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
     if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
     if (b == 0 || sq == 0) return ok();
     const int64_t nq = (int64_t(sq) + 127) / 128, nk = (int64_t(sk) + 127) / 128;
     if (std::max(nq, nk) * 128 * d * 2 >= kMaxSliceBytes)
-        return fail(MHA_ERR_OVERFLOW, "fp8: one (batch, head) slice of codes spans >= 2^31 bytes");
+        return fail(MHA_ERR_OVERFLOW, "%s: one (batch, head) slice of codes spans >= 2^31 bytes", name);
     const int64_t nwg = int64_t(b) * hq * nq;
     const int64_t nquant = int64_t(b) * (hq * nq + 2 * hk * nk);
     if (nwg > INT32_MAX || nquant > INT32_MAX)
-        return fail(MHA_ERR_OVERFLOW, "fp8: grid exceeds 2^31-1 workgroups");
+        return fail(MHA_ERR_OVERFLOW, "%s: grid exceeds 2^31-1 workgroups", name);
 
     size_t off[6];
-    mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, off);
+    if (mx)
+        mha_mxfp8_workspace_layout(b, hq, hk, sq, sk, d, off);
+    else
+        mha_fp8_workspace_layout(b, hq, hk, sq, sk, d, off);
     char* wsb = static_cast<char*>(ws);
     auto quant = [&](const void* src, const mha::View& sv, const float* mean, int heads, int s, int64_t nblk,
-                     size_t code_off, size_t scale_off, bool widen) {
+                     size_t code_off, int64_t scale_off, bool widen) {
         mha::QuantParams qp{};
         qp.src = src;
         qp.sv = sv;
@@ -347,13 +382,24 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
         qp.d = d;
         qp.nblk = static_cast<int>(nblk);
         qp.codes = reinterpret_cast<uint8_t*>(wsb + code_off);
-        qp.scales = reinterpret_cast<float*>(wsb + scale_off);
+        qp.mx = mx;
+        if (mx)   // per-row exponents (V: none stored, its values carry them)
+            qp.exps = scale_off >= 0 ? reinterpret_cast<uint8_t*>(wsb + scale_off) : nullptr;
+        else
+            qp.scales = reinterpret_cast<float*>(wsb + scale_off);
         qp.widen = widen;
         return qp;
     };
-    const mha::QuantParams qq = quant(q, qv, nullptr, hq, sq, nq, off[0], off[3], false);
-    const mha::QuantParams qk = quant(k, kv, k_mean, hk, sk, nk, off[1], off[4], false);
-    const mha::QuantParams qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], off[5], true);
+    mha::QuantParams qq, qk, qvv;
+    if (mx) {
+        qq = quant(q, qv, nullptr, hq, sq, nq, off[0], int64_t(off[3]), false);
+        qk = quant(k, kv, k_mean, hk, sk, nk, off[1], int64_t(off[4]), false);
+        qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], -1, true);
+    } else {
+        qq = quant(q, qv, nullptr, hq, sq, nq, off[0], int64_t(off[3]), false);
+        qk = quant(k, kv, k_mean, hk, sk, nk, off[1], int64_t(off[4]), false);
+        qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], int64_t(off[5]), true);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = mha::launch_quant_fp8(qq, qk, qvv, s);
     if (e != hipSuccess) return hip_status(e, "quant_fp8 launch");
@@ -365,6 +411,10 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     p.q_scale = qq.scales;
     p.k_scale = qk.scales;
     p.v_scale = qvv.scales;
+    if (mx) {
+        p.q_exps = qq.exps;
+        p.k_exps = qk.exps;
+    }
     p.o = o;
     p.ov = ov;
     p.lse = lse;
@@ -379,6 +429,26 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_s
     p.n_mblocks = static_cast<int>(nq);
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
     return hip_status(mha::launch_attn_fwd_fp8(p, d, causal != 0, s), "attn_fwd_fp8 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_fwd_fp8(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
+                       mha_strides v_stride, const float* k_mean, void* o, mha_strides o_stride, float* lse, int b,
+                       int hq, int hk, int sq, int sk, int d, float softmax_scale, int causal, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return fwd_quantised(false, q, q_stride, k, k_stride, v, v_stride, k_mean, o, o_stride, lse, b, hq, hk, sq, sk, d,
+                         softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+mha_status mha_fwd_mxfp8(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
+                         mha_strides v_stride, const float* k_mean, void* o, mha_strides o_stride, float* lse, int b,
+                         int hq, int hk, int sq, int sk, int d, float softmax_scale, int causal, void* ws,
+                         size_t ws_bytes, void* stream) {
+    return fwd_quantised(true, q, q_stride, k, k_stride, v, v_stride, k_mean, o, o_stride, lse, b, hq, hk, sq, sk, d,
+                         softmax_scale, causal, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,18 @@
 // stored widened to bf16 instead (E4M3 values are exactly representable), which
 // is the form the P.V MFMA consumes.  HBM-bound: 2 bytes read and 1 byte (V: 2)
 // written per element.
+//
+// MXFP8 (the MXFP8 hd128 recipe of the first page's commit message table, with
+// the uint8 E8M0 per-1x32 descales of the second page's review comments; block
+// format of OCP Microscaling v1.0): instead of one fp32 scale per 128 tokens,
+// every 32 channels of a token row share an exponent
+//   E      = clamp(floor(log2(amax)) - 8, -127, 127), read from amax's exponent
+//            field (8 = exponent of E4M3's largest normal, 448 = 1.75 * 2^8);
+//            rows of zeros (and subnormal amax) take E = -127, byte 0
+//   code   = E4M3(x * 2^-E), the product exact, saturated at +-448
+// stored as the byte E + 127 in [b, h, nblk*128, D/32].  V is stored as
+// decode(code) * 2^E in bf16 (exact while it stays in bf16's normal range),
+// so the attention kernel needs no V scale at all.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -26,6 +38,54 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int TOK = 128;
+
+// MXFP8: every thread holds 8 channels of PASSES token rows; the 4 threads of a 32-channel
+// block are adjacent lanes, so the block max takes two lane exchanges.
+template <int D, int PASSES>
+__device__ __forceinline__ void quant_rows_mx(const QuantParams& p, const float (&x)[PASSES][8], int bh, int blk,
+                                              int r0, int c0) {
+    constexpr int ROWS = TOK / PASSES;
+    const int64_t row0 = static_cast<int64_t>(bh) * p.nblk * TOK + blk * TOK;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[ps][i]));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const int field = static_cast<int>(__float_as_uint(m) >> 23);     // m >= 0: no sign bit
+        const int e = field == 0 ? -127 : max(field - 127 - 8, -127);     // at most 254 - 135 = 119
+        const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);   // 2^-e, normal
+        const float up = e > -127 ? __uint_as_float(static_cast<uint32_t>(127 + e) << 23) : 0x1p-127f;
+        uint32_t packed[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[ps][half * 4 + j] * inv, -448.f), 448.f);
+            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wv, true);
+            packed[half] = static_cast<uint32_t>(wv);
+        }
+        const int64_t row = row0 + ps * ROWS + r0;
+        if (p.widen) {
+            // decode(code) * 2^e, exact in fp32 and (in bf16's normal range) in bf16
+            uint32_t wide[4];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed[half]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed[half]), true);
+                wide[2 * half] = pack_bf16x2(lo[0] * up, lo[1] * up);
+                wide[2 * half + 1] = pack_bf16x2(hi[0] * up, hi[1] * up);
+            }
+            *reinterpret_cast<u32x4*>(p.codes + (row * D + c0) * 2) = u32x4{wide[0], wide[1], wide[2], wide[3]};
+        } else {
+            *reinterpret_cast<u32x2*>(p.codes + row * D + c0) = u32x2{packed[0], packed[1]};
+        }
+        if (p.exps != nullptr && (c0 & 31) == 0)
+            p.exps[row * (D / 32) + c0 / 32] = static_cast<uint8_t>(e + 127);
+    }
+}
 
 // Workgroup ids run over heads fastest, then token blocks, then batches: workgroups that are
 // dispatched together read neighbouring 2*D-byte pieces of the same BSHD token rows.
@@ -71,6 +131,10 @@ __device__ __forceinline__ void quant_block(const QuantParams& p, int id, float*
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ps][i]));
+    }
+    if (p.mx) {
+        quant_rows_mx<D, PASSES>(p, x, bh, blk, r0, c0);
+        return;
     }
     // block max: within the wave, then across the 4 waves through LDS
 #pragma unroll

@@ -1,11 +1,13 @@
 /*
  * mha.h - C ABI of the MI355X (gfx950) fused attention forward library (libmha.so).
  *
- * Three operations, each enqueued on the caller's HIP stream:
+ * Operations, each enqueued on the caller's HIP stream:
  *
  *   mha_fwd_bf16   fused attention forward, bf16 in / bf16 out, fp32 accumulate
+ *   mha_fwd_bf16_varlen  the same over packed sequences (cumulative offsets)
  *   k_smooth_mean  per-(batch, kv head) K mean behind a gate (two kernels, one call)
  *   mha_fwd_fp8    K-smoothed FP8 (E4M3) block-quantised attention forward
+ *   mha_fwd_mxfp8  the same with MXFP8 (E8M0 exponent per 32 channels) quantisation
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -210,6 +212,45 @@ mha_status mha_fwd_fp8(const void* q, mha_strides q_stride,
                        int b, int hq, int hk, int sq, int sk, int d,
                        float softmax_scale, int causal,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mha_fwd_mxfp8 - the same quantised call with the MXFP8 hd128 recipe of
+ * "[HIP] Mha v4: run the K-smoothing gate as one HIP call" (commit message
+ * table) and its uint8 E8M0 per-1x32 descales ("MHA v4: fixes, refactor, new
+ * kernel, perf tweaks", review comments), in the block format of OCP
+ * Microscaling v1.0.  Arguments, layouts and errors as mha_fwd_fp8; the
+ * workspace is sized by mha_fwd_mxfp8_workspace_bytes().
+ *
+ * Steps: x as for mha_fwd_fp8 (K smoothed by k_mean); every 32 channels of a
+ * token row share an exponent E = clamp(floor(log2(amax)) - 8, -127, 127)
+ * (E = -127 for a block of zeros), code = E4M3(x * 2^-E) (round to nearest
+ * even, saturating at +-448).  Scores come from the fp8 MFMA with the Q and K
+ * exponents as its per-block scale operands, so no fp32 rescaling follows;
+ * V is kept as decode(code) * 2^E in bf16 (exact while in bf16's normal
+ * range) and P.V runs on bf16 MFMA with P rounded to bf16.
+ *
+ * Workspace layout (byte offsets from ws, 256-byte aligned regions):
+ *   q codes  uint8 [b, hq, nblk_q*128, d]    (token-padded, zero-filled tail)
+ *   k codes  uint8 [b, hk, nblk_k*128, d]
+ *   v values bf16  [b, hk, nblk_k*128, d]    (decode(code) * 2^E)
+ *   q exps   uint8 [b, hq, nblk_q*128, d/32] (E8M0 bytes E + 127; tail rows 0)
+ *   k exps   uint8 [b, hk, nblk_k*128, d/32]
+ */
+size_t mha_fwd_mxfp8_workspace_bytes(int b, int hq, int hk, int sq, int sk, int d);
+
+/* Byte offsets of the five regions above, in the order listed; MHA_ERR_SHAPE for
+ * invalid sizes (d must be a positive multiple of 32). `offsets` is a host array of 5. */
+mha_status mha_mxfp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets);
+
+mha_status mha_fwd_mxfp8(const void* q, mha_strides q_stride,
+                         const void* k, mha_strides k_stride,
+                         const void* v, mha_strides v_stride,
+                         const float* k_mean,
+                         void* o, mha_strides o_stride,
+                         float* lse,
+                         int b, int hq, int hk, int sq, int sk, int d,
+                         float softmax_scale, int causal,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* mha_status_string(mha_status status);

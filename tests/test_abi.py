@@ -170,3 +170,35 @@ def test_fp8_refusals_and_layout(lib):
     assert call(wsb=1024)[0] == 6
     assert call(mean=FAKE + 2)[0] == 4
     assert call(hq=3)[0] == 2
+
+
+def test_mxfp8_refusals_and_layout(lib):
+    off = mha.mha_mxfp8_workspace_layout(1, 16, 16, 4096, 4096, 128)
+    assert len(off) == 5 and off[0] == 0 and all(o % 256 == 0 for o in off)
+    assert off[1] - off[0] >= 16 * 4096 * 128 and off[2] - off[1] >= 16 * 4096 * 128
+    assert off[3] - off[2] >= 16 * 4096 * 128 * 2 and off[4] - off[3] >= 16 * 4096 * 4
+    need = lib.mha_fwd_mxfp8_workspace_bytes(1, 16, 16, 4096, 4096, 128)
+    assert need >= off[4] + 16 * 4096 * 4
+    with pytest.raises(mha.MhaError):
+        mha.mha_mxfp8_workspace_layout(1, 16, 16, 4096, 4096, 100)   # d not a multiple of 32
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, mean=None, o=FAKE, lse=None, b=1, hq=2, hk=2, sq=256, sk=256, d=128,
+                 scale=0.088, causal=0, ws=FAKE, wsb=lib.mha_fwd_mxfp8_workspace_bytes(1, 2, 2, 256, 256, 128))
+        a.update(kw)
+        st_ = _bshd(256, 2, 128)
+        st = lib.mha_fwd_mxfp8(a["q"], st_, a["k"], st_, a["v"], st_, a["mean"], a["o"], st_, a["lse"], a["b"],
+                               a["hq"], a["hk"], a["sq"], a["sk"], a["d"], a["scale"], a["causal"], a["ws"],
+                               a["wsb"], None)
+        return st, lib.mha_last_error().decode()
+
+    assert call(d=64)[0] == 3 and "mxfp8" in call(d=64)[1]
+    assert call(v=None)[0] == 1
+    assert call(ws=None)[0] == 6
+    assert call(ws=FAKE + 64)[0] == 6
+    # the fp8 workspace is smaller than the mxfp8 one: refused
+    assert call(wsb=lib.mha_fwd_fp8_workspace_bytes(1, 2, 2, 256, 256, 128))[0] == 6
+    assert call(mean=FAKE + 2)[0] == 4
+    assert call(hq=3)[0] == 2
+    assert call(scale=float("nan"))[0] != 0
+    assert call(b=0)[0] == 0 and call(sq=0)[0] == 0

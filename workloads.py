@@ -40,6 +40,7 @@ class Workload:
     seed: int
     fp8: bool = False
     k_bias_std: float = 0.0  # per-(head, channel) K bias, FP8 smoothing workload only
+    mx: bool = False         # quantised with the MXFP8 recipe (fp8 must be set too)
     description: str = ""
 
     @property
@@ -87,6 +88,10 @@ WORKLOADS = {
         "fp8_long_h5", b=1, hq=5, hk=5, sq=65536, sk=65536, d_qk=128, d_v=128, causal=False,
         seed=109, fp8=True, k_bias_std=3.0,
         description="b1 h5 65536^2 d128 non-causal, bf16 in, K smoothed, e4m3 compute, bf16 out"),
+    "mxfp8_ksmooth_d128": Workload(
+        "mxfp8_ksmooth_d128", b=1, hq=16, hk=16, sq=4096, sk=4096, d_qk=128, d_v=128, causal=False,
+        seed=111, fp8=True, k_bias_std=3.0, mx=True,
+        description="b1 h16 4096^2 d128 non-causal, bf16 in, K smoothed, MXFP8 (E8M0 per 32 channels), bf16 out"),
 }
 
 

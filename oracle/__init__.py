@@ -31,6 +31,8 @@ Modules:
                on the dequantised, smoothed tensors (the algorithm's steps).
   mx         - MXFP8: E4M3 elements with one E8M0 exponent per 32 channels,
                and attention on the dequantised, smoothed tensors.
+  window     - sliding-window attention with per-head sink logits (plain
+               definition).
 
 Every function is pinned by a ``-m "not gpu"`` test against facts fixed
 outside this package: closed forms, hand-derived examples under
@@ -49,3 +51,4 @@ from .fp8 import (  # noqa: F401
     fp8_attention_forward,
 )
 from .mx import mx_quantize, mx_dequantize, mxfp8_attention_forward  # noqa: F401
+from .window import attention_window_sink, visible_mask, visible_pairs  # noqa: F401

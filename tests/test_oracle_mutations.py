@@ -242,3 +242,55 @@ def test_mx_source_passes_pins():
 @pytest.mark.parametrize("name,old,new", MX_MUTANTS, ids=[m[0] for m in MX_MUTANTS])
 def test_mx_mutant_is_caught(name, old, new):
     assert not _mx_pins_pass(_load_mx(old, new))
+
+
+# ---------------------------------------------------------------- window / sink pins
+
+def _window_pins_pass(mod):
+    import test_oracle_window as tw
+    try:
+        g = _golden("window_sink_worked_examples.json")
+        for c in g["cases"]:
+            sinks = None if c["sink"] is None else np.array([c["sink"]])
+            o, lse = mod.attention_window_sink(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]), scale=1.0,
+                                               causal=c["causal"], window_left=c["window_left"],
+                                               window_right=c["window_right"], sinks=sinks)
+            if not (np.allclose(o[0, :, 0, 0], c["o"], rtol=0, atol=1e-13)
+                    and np.allclose(lse[0, 0], c["lse"], rtol=0, atol=1e-13)):
+                return False
+        for causal, left, right in ((True, 3, -1), (False, 2, 1)):
+            q, k, v = RNG.standard_normal((1, 7, 4, 3)), RNG.standard_normal((1, 9, 2, 3)), RNG.standard_normal((1, 9, 2, 2))
+            sinks = RNG.standard_normal(4)
+            o, lse = mod.attention_window_sink(q, k, v, scale=0.7, causal=causal, window_left=left, window_right=right,
+                                               sinks=sinks)
+            o_b, lse_b = tw._brute(q, k, v, 0.7, causal, left, right, sinks)
+            if not (np.allclose(o, o_b, rtol=0, atol=1e-12) and np.allclose(lse, lse_b, rtol=0, atol=1e-12)):
+                return False
+        o, lse = mod.attention_window_sink(np.ones((1, 2, 1, 2)), np.zeros((1, 0, 1, 2)), np.zeros((1, 0, 1, 2)),
+                                           scale=1.0, causal=False, sinks=np.array([0.5]))
+        if not (np.all(o == 0) and np.all(lse == 0.5)):
+            return False
+    except Exception:
+        return False
+    return True
+
+
+WINDOW_MUTANTS = [
+    ("left_off_by_one", "vis &= j >= i - window_left", "vis &= j > i - window_left"),
+    ("right_off_by_one", "vis &= j <= i + window_right", "vis &= j <= i + window_right + 1"),
+    ("sink_not_in_denominator", "denom = p.sum(axis=1) + np.exp(sink - m_safe)", "denom = p.sum(axis=1)"),
+    ("sink_scaled", "sink = -np.inf if sinks is None else float(sinks[h])",
+     "sink = -np.inf if sinks is None else float(sinks[h]) * scale"),
+    ("sink_per_kv_head", "sink = -np.inf if sinks is None else float(sinks[h])",
+     "sink = -np.inf if sinks is None else float(sinks[g])"),
+    ("sink_not_in_max", "m = np.maximum(s.max(axis=1, initial=-np.inf), sink)", "m = s.max(axis=1, initial=-np.inf)"),
+]
+
+
+def test_window_source_passes_pins():
+    assert _window_pins_pass(_load("window.py"))
+
+
+@pytest.mark.parametrize("name,old,new", WINDOW_MUTANTS, ids=[m[0] for m in WINDOW_MUTANTS])
+def test_window_mutant_is_caught(name, old, new):
+    assert not _window_pins_pass(_load("window.py", old, new))

@@ -97,7 +97,10 @@ def cpu_baseline(w, q, k, v, budget_s=12.0, max_heads=64):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    import workloads
     grp = w.hq // w.hk
+    sinks = workloads.make_sinks(w)
+    ext = w.window_left >= 0 or w.window_right >= 0 or sinks is not None
     flops, elapsed, heads = 0.0, 0.0, 0
     for h in range(min(max_heads, w.hq)):
         g = h // grp
@@ -105,9 +108,14 @@ def cpu_baseline(w, q, k, v, budget_s=12.0, max_heads=64):
         kh = k[0:1, :, g:g + 1].float().numpy()
         vh = v[0:1, :, g:g + 1].float().numpy()
         t0 = time.perf_counter()
-        oracle.attention_forward(qh, kh, vh, scale=w.scale, causal=w.causal)
+        if ext:
+            oracle.attention_window_sink(qh, kh, vh, scale=w.scale, causal=w.causal, window_left=w.window_left,
+                                         window_right=w.window_right,
+                                         sinks=None if sinks is None else sinks[h:h + 1].double().numpy())
+        else:
+            oracle.attention_forward(qh, kh, vh, scale=w.scale, causal=w.causal)
         elapsed += time.perf_counter() - t0
-        flops += oracle.attention_flops(1, 1, w.sq, w.sk, w.d_qk, w.d_v, w.causal)
+        flops += w.flops() / (w.b * w.hq)
         heads += 1
         if elapsed >= budget_s:
             break
@@ -226,8 +234,16 @@ def main():
     lse = torch.empty((w.b, w.hq, w.sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        mha.mha_fwd_bf16(q, k, v, causal=w.causal, softmax_scale=w.scale, out=o)
+    sinks = workloads.make_sinks(w)
+    if w.window_left >= 0 or w.window_right >= 0 or sinks is not None:
+        sinks_d = None if sinks is None else sinks.to(dev)
+
+        def step():
+            mha.mha_fwd_bf16_window_sink(q, k, v, causal=w.causal, window_left=w.window_left,
+                                         window_right=w.window_right, sinks=sinks_d, softmax_scale=w.scale, out=o)
+    else:
+        def step():
+            mha.mha_fwd_bf16(q, k, v, causal=w.causal, softmax_scale=w.scale, out=o)
 
     torch.cuda.synchronize()
     ms, wall = time_launches(step, a.steps, a.warmup, stream)

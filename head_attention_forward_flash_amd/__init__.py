@@ -31,7 +31,7 @@ STATUS_NAMES = {
 
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = (
-    "mha_fwd_bf16", "mha_fwd_bf16_varlen", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
+    "mha_fwd_bf16", "mha_fwd_bf16_varlen", "mha_fwd_bf16_window_sink", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
     "mha_fwd_mxfp8", "mha_status_string", "mha_last_error",
 )
@@ -66,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_fwd_bf16_varlen.restype = i32
     lib.mha_fwd_bf16_varlen.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp, vp, vp,
                                         i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.mha_fwd_bf16_window_sink.restype = i32
+    lib.mha_fwd_bf16_window_sink.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
+                                             i32, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp]
     lib.k_smooth_mean_workspace_bytes.restype = sz
     lib.k_smooth_mean_workspace_bytes.argtypes = [i32] * 6
     lib.k_smooth_mean.restype = i32
@@ -147,6 +150,33 @@ def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] =
     _check(lib.mha_fwd_bf16(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
                             _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
                             float(softmax_scale), int(bool(causal)), _stream(q.device)))
+    return out, lse_t
+
+
+def mha_fwd_bf16_window_sink(q, k, v, causal: bool = False, window_left: int = -1, window_right: int = -1,
+                             sinks=None, softmax_scale: Optional[float] = None, out=None, lse: bool = True):
+    """mha_fwd_bf16 with a sliding window (-1 = unbounded side) and per-head sink logits
+    (fp32 [hq] on the device, or None). Returns (o, lse)."""
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, out, sinks)
+    b, sq, hq, d_qk = q.shape
+    _, sk, hk, _ = k.shape
+    d_v = v.shape[3]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 tensor of hq elements")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((b, sq, hq, d_v), dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
+    _check(lib.mha_fwd_bf16_window_sink(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v),
+                                        _bshd_strides(v), _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq,
+                                        sk, d_qk, d_v, float(softmax_scale), int(bool(causal)), int(window_left),
+                                        int(window_right), _ptr(sinks), _stream(q.device)))
     return out, lse_t
 
 

@@ -84,11 +84,14 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 // 128-row workgroups run two per CU; the 256-row one runs alone with 8 waves, which halves
 // the K/V traffic per FLOP of the wide d192/d128 tiles.
 template <int DQK, int DV> struct TileCfg;
+template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
 
-template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED>
+// EXT: sliding window (keys j with i - window_left <= j <= i + window_right) and per-head sink
+// logits, for dense (not packed) inputs.
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
     constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
@@ -126,6 +129,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     //      (PAIRED): a workgroup takes block n-1-j and then block j, so every workgroup does
     //      the same work and the grid has no tail of light workgroups.
     static_assert(CAUSAL || !PAIRED, "only causal blocks differ in work");
+    static_assert(!EXT || (!VARLEN && !PAIRED), "windows and sinks run on dense, unpaired grids");
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
@@ -202,7 +206,12 @@ next_item:
         }
         const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
 
-        const int kv_end = CAUSAL ? min(sk, (mblk + 1) * BM) : sk;
+        int kv_end = CAUSAL ? min(sk, (mblk + 1) * BM) : sk;
+        int t0 = 0;   // first key tile: keys left of every row's window are never loaded
+        if constexpr (EXT) {
+            if (!CAUSAL && p.window_right >= 0) kv_end = min(sk, (mblk + 1) * BM + p.window_right);
+            if (p.window_left >= 0) t0 = max(0, mblk * BM - p.window_left) / BN;
+        }
         const int ntiles = (kv_end + BN - 1) / BN;
 
         // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
@@ -214,10 +223,13 @@ next_item:
         //      The per-lane global offsets are loop-invariant; each tile's buffer descriptor is
         //      based at the tile and bounded by the slice, so keys past sk land as zeros.
         auto kswz = [](int r) __attribute__((always_inline)) {
-            return KROWB % 256 == 0 ? (r & 15) : ((r >> 1) & 7);    // rows of 256 B, else 128/384 B
+            // rows of 256 B; of 64 B (4 chunks: the 16 rows of a read fall on 4 row pairs mod 4);
+            // else 128/384 B
+            return KROWB % 256 == 0 ? (r & 15) : KROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
         };
         auto vswz = [](int r) __attribute__((always_inline)) {
-            return VROWB % 256 == 0 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+            // 64-B rows: the 4 keys a transposing read touches are 256 contiguous bytes already
+            return VROWB % 256 == 0 ? ((r & 3) << 2) : VROWB == 64 ? 0 : (((r >> 1) & 1) << 2);
         };
         uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
@@ -295,16 +307,27 @@ next_item:
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
             }
         };
-        // ---- scores of keys past sk, or above the diagonal, become -inf (block u = keys 32u ..)
+        // ---- scores of keys past sk, above the diagonal or outside the window become -inf
+        //      (block u = keys 32u ..)
         auto need_mask = [&](int u) __attribute__((always_inline)) {
             const int key0 = u * 32;
-            return (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
+            bool m = (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
+            if constexpr (EXT) {
+                m = m || (p.window_left >= 0 && key0 < wave_row0 + 31 - p.window_left) ||
+                    (!CAUSAL && p.window_right >= 0 && key0 + 31 > wave_row0 + p.window_right);
+            }
+            return m;
         };
         auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                if (key >= sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
+                bool out = key >= sk || (CAUSAL && key > my_row);
+                if constexpr (EXT) {
+                    out = out || (p.window_left >= 0 && key < my_row - p.window_left) ||
+                          (!CAUSAL && p.window_right >= 0 && key > my_row + p.window_right);
+                }
+                if (out) s[j] = kNegInf;
             }
         };
         // ---- this lane's max over its 16 scores of a block
@@ -463,19 +486,19 @@ next_item:
             pv_block(v_slot(Cur{}), 1, pf);
         };
 
-        if (ntiles > 0) {
+        if (ntiles > t0) {
             using Zero = std::integral_constant<int, 0>;
             using One = std::integral_constant<int, 1>;
-            issue_k(0, k_slot(Zero{}));
-            issue_v(0, v_slot(Zero{}));
-            issue_k(1, k_slot(One{}));
-            __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
+            issue_k(t0, k_slot(Zero{}));
+            issue_v(t0, v_slot(Zero{}));
+            issue_k(t0 + 1, k_slot(One{}));
+            __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_t0 has landed
             __syncthreads();
             f32x16 s;
             qk_block(k_slot(Zero{}), 0, s);
-            if (need_mask(0)) mask_block(0, s);
+            if (need_mask(2 * t0)) mask_block(2 * t0, s);
             float mx = lane_max(s);
-            int t = 0;
+            int t = t0;
             for (; t + 2 < ntiles; t += 2) {
                 iteration(t, Zero{}, s, mx);
                 iteration(t + 1, One{}, s, mx);
@@ -489,8 +512,23 @@ next_item:
         }
 
         // ---- epilogue: normalise, store O (bf16) and LSE
-        const float l_tot = l_run + swap_halves(l_run);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float l_tot = l_run + swap_halves(l_run);
+        float m_log2 = m_run * c;   // the reference max in base-2 units (c > 0 keeps -inf)
+        float o_scale = 1.f;
+        if constexpr (EXT) {
+            // the head's sink logit joins the normaliser: rebase both terms on their larger
+            // exponent so that neither overflows
+            if (p.sinks != nullptr) {
+                const float s2 = p.sinks[h] * kLog2e;
+                const float top = fmaxf(m_log2, s2);
+                if (top != kNegInf) {
+                    o_scale = m_log2 == kNegInf ? 0.f : fast_exp2(m_log2 - top);
+                    l_tot = l_tot * o_scale + fast_exp2(s2 - top);
+                    m_log2 = top;
+                }
+            }
+        }
+        const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
         if (my_row < sq) {
             uint16_t* orow = static_cast<uint16_t*>(p.o) + (orow0 + h * p.ov.sh + my_row * p.ov.ss);
 #pragma unroll
@@ -504,7 +542,7 @@ next_item:
                 }
             }
             if (p.lse != nullptr && half == 0) {
-                const float lse = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
+                const float lse = l_tot > 0.f ? (m_log2 + __log2f(l_tot)) * kLn2 : kNegInf;
                 p.lse[lse0 + my_row] = lse;
             }
         }
@@ -529,10 +567,18 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     // Pair causal query blocks when the grid fills the device a few times at most; on longer
     // grids the hardware's dispatch already overlaps short and long workgroups (measured:
     // pairing gains 5-10% on 2-8 rounds, nothing on 16).
+    const bool ext = p.window_left >= 0 || (!CAUSAL && p.window_right >= 0) || p.sinks != nullptr;
+    if (ext) {
+        if (VARLEN) return hipErrorInvalidValue;
+        if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, false, true>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0, stream, p);
+        return hipGetLastError();
+    }
     bool paired = false;
     if (CAUSAL && p.n_mblocks > 1) {
         int groups = 0;
-        const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL>;
+        const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false>;
         const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2, &groups);
         if (e != hipSuccess) return e;
         paired = blocks <= 8 * static_cast<int64_t>(groups);
@@ -540,10 +586,10 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     const int64_t nwg = paired ? static_cast<int64_t>(p.b) * p.hq * ((p.n_mblocks + 1) / 2) : blocks;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
     if (paired) {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL>), dim3(static_cast<unsigned>(nwg)),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false>), dim3(static_cast<unsigned>(nwg)),
                            dim3(BM * 2), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false>), dim3(static_cast<unsigned>(nwg)),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, false>), dim3(static_cast<unsigned>(nwg)),
                            dim3(BM * 2), 0, stream, p);
     }
     return hipGetLastError();
@@ -551,6 +597,8 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
 
 template <bool VARLEN>
 hipError_t launch_dims(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
+    if (d_qk == 32 && d_v == 32)
+        return causal ? launch<32, 32, true, VARLEN>(p, stream) : launch<32, 32, false, VARLEN>(p, stream);
     if (d_qk == 64 && d_v == 64)
         return causal ? launch<64, 64, true, VARLEN>(p, stream) : launch<64, 64, false, VARLEN>(p, stream);
     if (d_qk == 128 && d_v == 128)

@@ -30,6 +30,10 @@ struct AttnParams {
     const int* cu_q = nullptr;
     const int* cu_k = nullptr;
     int total_q = 0, total_k = 0;
+    // sliding window (dense inputs only): query i sees keys i - window_left .. i + window_right,
+    // -1 = unbounded on that side; per-query-head sink logits [hq] (nullptr = none)
+    int window_left = -1, window_right = -1;
+    const float* sinks = nullptr;
 };
 
 // Workgroups of `kernel` (launched with `threads` threads, no dynamic LDS) that the current

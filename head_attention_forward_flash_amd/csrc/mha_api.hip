@@ -74,7 +74,8 @@ mha_status make_view(const char* name, const void* ptr, const mha_strides& st, i
 }
 
 bool supported_bf16(int dqk, int dv) {
-    return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+    return (dqk == 32 && dv == 32) || (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) ||
+           (dqk == 192 && dv == 128);
 }
 
 mha_status check_common(int b, int hq, int hk, int sq, int sk, float scale, int causal) {
@@ -109,14 +110,22 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
-                        const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
-                        int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
-                        int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mha_status fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
+                    mha_strides v_stride, void* o, mha_strides o_stride, float* lse, int b, int hq, int hk, int sq,
+                    int sk, int d_qk, int d_v, float softmax_scale, int causal, int window_left, int window_right,
+                    const float* sinks, void* stream) {
     mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
     if (st != MHA_OK) return st;
+    if (window_left < -1 || window_right < -1)
+        return fail(MHA_ERR_VALUE, "window_left = %d, window_right = %d: each must be >= -1 (-1 = unbounded)",
+                    window_left, window_right);
+    if (sinks && reinterpret_cast<uintptr_t>(sinks) % 4 != 0) return fail(MHA_ERR_LAYOUT, "sinks must be 4-byte aligned");
     if (!supported_bf16(d_qk, d_v))
-        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (64,64) (128,128) (192,128)",
+        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (32,32) (64,64) (128,128) (192,128)",
                     d_qk, d_v);
     // Empty problems need no memory: q/o may be NULL when there are no query rows, k/v when
     // there are no keys.
@@ -156,8 +165,33 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
     p.sk = sk;
     p.group = hq / hk;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    // a side of the window that reaches past every key is no bound at all
+    p.window_left = window_left >= sq ? -1 : window_left;
+    p.window_right = (causal || window_right >= sk) ? -1 : window_right;
+    p.sinks = sinks;
     return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
                       "attn_fwd_bf16 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                        const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                        int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
+                        int causal, void* stream) {
+    return fwd_bf16(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, b, hq, hk, sq, sk, d_qk, d_v,
+                    softmax_scale, causal, -1, -1, nullptr, stream);
+}
+
+mha_status mha_fwd_bf16_window_sink(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                                    const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                                    int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
+                                    int causal, int window_left, int window_right, const float* sinks,
+                                    void* stream) {
+    return fwd_bf16(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, b, hq, hk, sq, sk, d_qk, d_v,
+                    softmax_scale, causal, window_left, window_right, sinks, stream);
 }
 
 mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
@@ -171,7 +205,7 @@ mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* 
     mha_status st = check_common(b, hq, hk, max_seqlen_q, max_seqlen_k, softmax_scale, causal);
     if (st != MHA_OK) return st;
     if (!supported_bf16(d_qk, d_v))
-        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (64,64) (128,128) (192,128)",
+        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (32,32) (64,64) (128,128) (192,128)",
                     d_qk, d_v);
     const bool has_rows = b > 0 && total_q > 0 && max_seqlen_q > 0;
     if (b > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(MHA_ERR_NULL, "cu_seqlens_q / cu_seqlens_k is NULL");

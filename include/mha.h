@@ -5,6 +5,7 @@
  *
  *   mha_fwd_bf16   fused attention forward, bf16 in / bf16 out, fp32 accumulate
  *   mha_fwd_bf16_varlen  the same over packed sequences (cumulative offsets)
+ *   mha_fwd_bf16_window_sink  the same with a sliding window and attention sinks
  *   k_smooth_mean  per-(batch, kv head) K mean behind a gate (two kernels, one call)
  *   mha_fwd_fp8    K-smoothed FP8 (E4M3) block-quantised attention forward
  *   mha_fwd_mxfp8  the same with MXFP8 (E8M0 exponent per 32 channels) quantisation
@@ -79,7 +80,8 @@ typedef struct {
  *   q    [b, sq, hq, d_qk] bf16      k [b, sk, hk, d_qk] bf16
  *   v    [b, sk, hk, d_v]  bf16      o [b, sq, hq, d_v]  bf16 (written)
  *   lse  [b, hq, sq] fp32 contiguous (written), or NULL to skip it
- *   (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}
+ *   (d_qk, d_v) in {(32, 32), (64, 64), (128, 128), (192, 128)} (32: the small-head
+ *   "vd32" shapes of the same page's Test Result table)
  *   b, sq, sk >= 0; hq, hk >= 1; hq % hk == 0.  b == 0 or sq == 0 is a no-op.
  *   softmax_scale: any finite value (usually 1/sqrt(d_qk)).
  *   causal: 0 or 1.
@@ -97,6 +99,33 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride,
                         float* lse,
                         int b, int hq, int hk, int sq, int sk, int d_qk, int d_v,
                         float softmax_scale, int causal, void* stream);
+
+/*
+ * mha_fwd_bf16_window_sink - mha_fwd_bf16 with a sliding window and per-head
+ * attention sinks: the GPT-OSS "sink+sliding-window" shapes named in the Test
+ * Result section of "Tune MHA config & small-head pipeline pathology".
+ *
+ *   window_left, window_right  query i sees key j only if j >= i - window_left
+ *       and j <= i + window_right, on top of the causal rule; -1 leaves that
+ *       side unbounded (a 128-token causal window is window_left = 127);
+ *       values below -1 are refused (MHA_ERR_VALUE)
+ *   sinks  [hq] fp32 device array of per-query-head logits in the units of
+ *       the scaled scores, or NULL: each joins its head's softmax normaliser
+ *       without a value row, O_i = sum_j e^(s_ij - m) v_j / (sum_j e^(s_ij - m)
+ *       + e^(sink_h - m)), and LSE includes it; 4-byte aligned
+ * Everything else (shapes, layouts, errors) as mha_fwd_bf16.  Key tiles left of
+ * a query block's window are never loaded.  A row that sees no key gets O = 0
+ * and LSE = sink_h (-inf without sinks).
+ */
+mha_status mha_fwd_bf16_window_sink(const void* q, mha_strides q_stride,
+                                    const void* k, mha_strides k_stride,
+                                    const void* v, mha_strides v_stride,
+                                    void* o, mha_strides o_stride,
+                                    float* lse,
+                                    int b, int hq, int hk, int sq, int sk, int d_qk, int d_v,
+                                    float softmax_scale, int causal,
+                                    int window_left, int window_right, const float* sinks,
+                                    void* stream);
 
 /*
  * mha_fwd_bf16_varlen - mha_fwd_bf16 over a batch of packed sequences of

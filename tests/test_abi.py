@@ -202,3 +202,35 @@ def test_mxfp8_refusals_and_layout(lib):
     assert call(hq=3)[0] == 2
     assert call(scale=float("nan"))[0] != 0
     assert call(b=0)[0] == 0 and call(sq=0)[0] == 0
+
+
+def _window_sink(lib, **kw):
+    a = dict(q=FAKE, qs=_bshd(128, 2, 64), k=FAKE, ks=_bshd(128, 2, 64), v=FAKE, vs=_bshd(128, 2, 64),
+             o=FAKE, os=_bshd(128, 2, 64), lse=None, b=1, hq=2, hk=2, sq=128, sk=128, dqk=64, dv=64,
+             scale=0.125, causal=1, left=127, right=-1, sinks=None)
+    a.update(kw)
+    st = lib.mha_fwd_bf16_window_sink(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"], a["lse"],
+                                      a["b"], a["hq"], a["hk"], a["sq"], a["sk"], a["dqk"], a["dv"], a["scale"],
+                                      a["causal"], a["left"], a["right"], a["sinks"], None)
+    return st, lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(left=-2), 8, "window_left = -2"),
+    (dict(right=-5, causal=0), 8, "each must be >= -1"),
+    (dict(sinks=FAKE + 2), 4, "sinks must be 4-byte aligned"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(dqk=16, dv=16), 3, "(32,32)"),
+    (dict(causal=3), 8, "causal"),
+])
+def test_window_sink_refusals(lib, kw, status, needle):
+    st, msg = _window_sink(lib, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_window_sink_and_d32_empty_problems_are_noops(lib):
+    assert _window_sink(lib, b=0)[0] == 0
+    assert _window_sink(lib, sq=0, sinks=FAKE)[0] == 0
+    assert _bf16(lib, b=0, dqk=32, dv=32, qs=_bshd(128, 2, 32), ks=_bshd(128, 2, 32), vs=_bshd(128, 2, 32),
+                 os=_bshd(128, 2, 32))[0] == 0

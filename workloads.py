@@ -41,6 +41,9 @@ class Workload:
     fp8: bool = False
     k_bias_std: float = 0.0  # per-(head, channel) K bias, FP8 smoothing workload only
     mx: bool = False         # quantised with the MXFP8 recipe (fp8 must be set too)
+    window_left: int = -1    # sliding window (-1 = unbounded side)
+    window_right: int = -1
+    sink_std: float = 0.0    # per-query-head sink logits ~ N(0, sink_std^2) when > 0
     description: str = ""
 
     @property
@@ -48,9 +51,16 @@ class Workload:
         return 1.0 / math.sqrt(self.d_qk)
 
     def flops(self) -> float:
-        """Algorithmic attention FLOPs: 2*b*hq*sq*sk*(d_qk + d_v), halved when causal."""
-        f = 2.0 * self.b * self.hq * self.sq * self.sk * (self.d_qk + self.d_v)
-        return f / 2.0 if self.causal else f
+        """Algorithmic attention FLOPs: 2*(d_qk + d_v) per visible (query, key) pair and head:
+        2*b*hq*sq*sk*(d_qk + d_v), halved when causal; with a window, the pairs it keeps."""
+        if self.window_left < 0 and self.window_right < 0:
+            f = 2.0 * self.b * self.hq * self.sq * self.sk * (self.d_qk + self.d_v)
+            return f / 2.0 if self.causal else f
+        i = torch.arange(self.sq, dtype=torch.int64)
+        lo = (i - self.window_left).clamp(min=0) if self.window_left >= 0 else torch.zeros_like(i)
+        hi = i if self.causal else (i + self.window_right if self.window_right >= 0 else torch.full_like(i, self.sk - 1))
+        pairs = int((hi.clamp(max=self.sk - 1) - lo + 1).clamp(min=0).sum())
+        return 2.0 * self.b * self.hq * pairs * (self.d_qk + self.d_v)
 
 
 WORKLOADS = {
@@ -92,6 +102,19 @@ WORKLOADS = {
         "mxfp8_ksmooth_d128", b=1, hq=16, hk=16, sq=4096, sk=4096, d_qk=128, d_v=128, causal=False,
         seed=111, fp8=True, k_bias_std=3.0, mx=True,
         description="b1 h16 4096^2 d128 non-causal, bf16 in, K smoothed, MXFP8 (E8M0 per 32 channels), bf16 out"),
+    # GPT-OSS-like layers (64 query heads, 8 kv heads, head dim 64): the sliding-window layer
+    # (128-token causal window) and the full causal layer, both with per-head sinks
+    "gptoss_swa_sink_d64": Workload(
+        "gptoss_swa_sink_d64", b=1, hq=64, hk=8, sq=8192, sk=8192, d_qk=64, d_v=64, causal=True, seed=112,
+        window_left=127, sink_std=1.0,
+        description="b1 hq64 hk8 8192^2 d64 causal, 128-token sliding window, per-head sinks, bf16"),
+    "gptoss_sink_d64": Workload(
+        "gptoss_sink_d64", b=1, hq=64, hk=8, sq=8192, sk=8192, d_qk=64, d_v=64, causal=True, seed=113,
+        sink_std=1.0, description="b1 hq64 hk8 8192^2 d64 causal, per-head sinks, bf16"),
+    # the small-head "vd32" shape family (2048^2, 16/16 heads, head dim 32)
+    "vd32_noncausal": Workload(
+        "vd32_noncausal", b=1, hq=16, hk=16, sq=2048, sk=2048, d_qk=32, d_v=32, causal=False, seed=114,
+        description="b1 hq16 hk16 2048^2 d32 non-causal bf16"),
 }
 
 
@@ -116,6 +139,15 @@ def make_qkv(w: Workload, seed: Optional[int] = None, k_bias_std: Optional[float
         k32 = k32 + bias.view(1, 1, w.hk, w.d_qk)
     k = k32.to(torch.bfloat16)
     return q, k, v
+
+
+def make_sinks(w: Workload) -> Optional[torch.Tensor]:
+    """Seeded float32 [hq] sink logits of workload ``w`` (None when it has none)."""
+    if w.sink_std <= 0.0:
+        return None
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 1000)
+    return torch.randn((w.hq,), generator=gen, dtype=torch.float32) * w.sink_std
 
 
 def make_random(shape, seed: int, dtype=torch.bfloat16, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:

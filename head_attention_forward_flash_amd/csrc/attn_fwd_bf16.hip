@@ -133,8 +133,22 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
-    const int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
     const int per_head = PAIRED ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
+    int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
+    if constexpr (VARLEN) {
+        // Packed sequences differ in length, so contiguous eighths of the grid would give the
+        // XCDs very different work.  Deal (sequence, kv head) units round-robin instead: XCD x
+        // takes units x, x + 8, ... (every sequence, one kv head in eight, with its query heads
+        // and blocks kept together); units past the last full round of 8 keep their own ids.
+        const int unit = per_head * p.group;                 // workgroups per (sequence, kv head)
+        const int full = (nwg / unit / 8) * 8 * unit;
+        if (pid < full) {
+            const int i = pid >> 3;
+            lid = ((pid & 7) + 8 * (i / unit)) * unit + i % unit;
+        } else {
+            lid = pid;
+        }
+    }
     const int mrev = lid % per_head;
     const int bh = lid / per_head;
     int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first

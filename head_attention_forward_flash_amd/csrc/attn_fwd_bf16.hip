@@ -81,8 +81,8 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 }
 
 // Tile shape per head-dim pair: BM query rows per workgroup (32 per wave), BN keys per tile.
-// 128-row workgroups run two per CU; the 256-row one runs alone with 8 waves, which halves
-// the K/V traffic per FLOP of the wide d192/d128 tiles.
+// 128-row workgroups run two (d128) to four (d32) per CU; the 256-row one runs alone with 8
+// waves, which halves the K/V traffic per FLOP of the wide d192/d128 tiles.
 template <int DQK, int DV> struct TileCfg;
 template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };

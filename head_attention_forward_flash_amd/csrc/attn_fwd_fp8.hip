@@ -1,4 +1,4 @@
-// Attention forward on E4M3-quantised, K-smoothed inputs (d = 128), gfx950.
+// Attention forward on E4M3-quantised, K-smoothed inputs (d = 64 or 128), gfx950.
 //
 // The attention side of the FP8 hd128 mha_v4 recipe ("[HIP] Mha v4: run the
 // K-smoothing gate as one HIP call", Performance table; "MHA v4: fixes,
@@ -47,7 +47,6 @@ namespace {
 
 constexpr int BM = 128;          // query rows per workgroup = one Q scale block
 constexpr int BN = 64;           // keys per tile (half a K/V scale block)
-constexpr int D = 128;
 constexpr int NTHREADS = 256;
 constexpr float kRescaleThreshold = 8.0f;     // log2 units
 constexpr float kMinFactor = 1.17549435e-38f;   // FLT_MIN
@@ -74,7 +73,7 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
 
-template <bool CAUSAL, bool MX>
+template <int D, bool CAUSAL, bool MX>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
     constexpr int NWAVES = NTHREADS / 64;
     constexpr int KROWB = D;                  // bytes per K8 row
@@ -84,6 +83,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     constexpr int KDMA = KTILE / 1024 / NWAVES;   // 1 KiB DMA blocks per wave per tile
     constexpr int VDMA = VTILE / 1024 / NWAVES;
     constexpr int CBLK = D / 32;
+    constexpr int KS = D / 64;                // fp8 MFMA k-steps of 64 channels
+    constexpr int EB = D / 32;                // MXFP8 exponent bytes per row
     static_assert(KDMA * NWAVES * 1024 == KTILE && VDMA * NWAVES * 1024 == VTILE, "DMA blocks must cover the tiles");
     static_assert(2 * (KTILE + VTILE) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const float* k_scale = MX ? nullptr : p.k_scale + static_cast<int64_t>(bg) * p.nk;
     const float* v_scale = MX ? nullptr : p.v_scale + static_cast<int64_t>(bg) * p.nk;
     // MXFP8 exponents: 4 bytes per row (one per 32 channels), rows padded like the codes
-    const uint32_t exp_slice = static_cast<uint32_t>(p.nk) * BM * 4;
+    const uint32_t exp_slice = static_cast<uint32_t>(p.nk) * BM * EB;
     const auto kers = make_rsrc(MX ? p.k_exps + static_cast<int64_t>(bg) * exp_slice : nullptr, MX ? exp_slice : 0u);
 
     const int wave_row0 = mblk * BM + wave * 32;
@@ -139,9 +140,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     // Q8 fragment: two k-steps of 64 channels, 32 codes per lane each.  softmax(c*s) with
     // c < 0 equals softmax(|c| * (-s)): a negative scale flips the sign bits of Q (exact).
     const uint32_t qsign = p.scale_log2 < 0.f ? 0x80808080u : 0u;
-    i32x8 qf[2];
+    i32x8 qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         // plain fp8: channels [32h, 32h + 32) of the k-step; MXFP8: [16h, +16) and [32 + 16h, +16)
         const uint32_t off = static_cast<uint32_t>(my_row * D + ks * 64 + half * (MX ? 16 : 32));
         const u32x4 a = buffer_load_b128(qrs, off) ^ qsign;
@@ -150,19 +151,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     }
     const float cq = q_scale * fabsf(p.scale_log2);   // base-2 factor of this block's scores, >= 0
     // MXFP8: the E8M0 byte of each k-step's 32 channels of this lane's query, in bits 0-7
-    uint32_t qe[2] = {0u, 0u};
+    uint32_t qe[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qe[ks] = 0u;
+    // the row's EB exponent bytes (d128: 4, one dword; d64: 2)
+    auto exp_word = [&](__amdgpu_buffer_rsrc_t r, uint32_t row) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (EB == 4) return buffer_load_b32(r, row * 4);
+        else return buffer_load_b16(r, row * 2);
+    };
     if constexpr (MX) {
-        const uint32_t qslice_e = static_cast<uint32_t>(p.nq) * BM * 4;
+        const uint32_t qslice_e = static_cast<uint32_t>(p.nq) * BM * EB;
         const auto qers = make_rsrc(p.q_exps + static_cast<int64_t>(bh) * qslice_e, qslice_e);
-        const uint32_t w = buffer_load_b32(qers, static_cast<uint32_t>(my_row * 4));
-        qe[0] = w >> (8 * half);
-        qe[1] = w >> (8 * (2 + half));
+        const uint32_t w = exp_word(qers, static_cast<uint32_t>(my_row));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qe[ks] = w >> (8 * (2 * ks + half));
     }
     // MXFP8: the exponent words of this lane's key in the two 32-key blocks of tile t (zeros
     // past the padded key range)
     auto kexp_load = [&](int t) __attribute__((always_inline)) {
         const uint32_t key = static_cast<uint32_t>(t * BN + col);
-        return u32x2{buffer_load_b32(kers, key * 4), buffer_load_b32(kers, (key + 32) * 4)};
+        return u32x2{exp_word(kers, key), exp_word(kers, key + 32)};
     };
 
     const int kv_end = CAUSAL ? min(p.sk, (mblk + 1) * BM) : p.sk;
@@ -184,8 +192,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
 
     // ---- DMA layout (see the bf16 kernel): K8 rows of 128 B keep chunk c of row r at
     //      c ^ ((r >> 1) & 7); widened V rows of 256 B keep chunk c of key r at c ^ 4*(r & 3).
-    auto kswz = [](int r) __attribute__((always_inline)) { return (r >> 1) & 7; };
-    auto vswz = [](int r) __attribute__((always_inline)) { return (r & 3) << 2; };
+    // (d64: K8 rows of 64 B keep chunk c at c ^ ((r >> 2) & 3), V rows of 128 B at c ^ 4*((r >> 1) & 1))
+    auto kswz = [](int r) __attribute__((always_inline)) { return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3; };
+    auto vswz = [](int r) __attribute__((always_inline)) { return D == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2; };
     uint32_t kgo[KDMA], vgo[VDMA];
 #pragma unroll
     for (int i = 0; i < KDMA; ++i) {
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         const uint8_t* row = kl + (kb * 32 + col) * KROWB;
         s = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             // 16-byte chunks of the row in Q's channel order (see the Q fragment)
             const int c0 = (MX ? ks * 4 + half : ks * 4 + half * 2) ^ kx;
             const int c1 = (MX ? ks * 4 + half + 2 : ks * 4 + half * 2 + 1) ^ kx;
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
     static_assert(VM_PROLOGUE < 16, "vmcnt immediate");
     constexpr int WAIT_K0 = VM_PROLOGUE | 0x0F70;
-    // region A: S of the next block (2 fp8 MFMAs, 4 K reads) under the exponentials of the
+    // region A: S of the next block (D/64 fp8 MFMAs, two K reads each) under the exponentials of the
     //           current block
     auto region_a = [&](const uint8_t* kl, int kb, uint32_t ke, f32x16& sn, const f32x16& s, float c, float bias,
                         bf16x8 (&pf)[2]) __attribute__((always_inline)) {
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         // keep the exponentials here: without a use inside the region the compiler would sink
         // them to the P.V MFMAs that consume them
         asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-        sched_region<2, 4, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, 2>{});
+        sched_region<KS, 2 * KS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KS>{});
         __builtin_amdgcn_sched_barrier(0);
     };
     // region B: P.V of the current block under its row sum and the next block's row max
@@ -492,15 +501,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
 }  // namespace
 
 hipError_t launch_attn_fwd_fp8(const Fp8AttnParams& p, int d, bool causal, hipStream_t stream) {
-    if (d != D) return hipErrorInvalidValue;
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
     const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
     if (nwg == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(nwg));
     const bool mx = p.q_exps != nullptr;
-    if (mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, true>), grid, dim3(NTHREADS), 0, stream, p);
-    if (mx && !causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, true>), grid, dim3(NTHREADS), 0, stream, p);
-    if (!mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, false>), grid, dim3(NTHREADS), 0, stream, p);
-    if (!mx && !causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, false>), grid, dim3(NTHREADS), 0, stream, p);
+    auto go = [&](auto d_c) {
+        constexpr int DD = decltype(d_c)::value;
+        if (mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DD, true, true>), grid, dim3(NTHREADS), 0, stream, p);
+        if (mx && !causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DD, false, true>), grid, dim3(NTHREADS), 0, stream, p);
+        if (!mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DD, true, false>), grid, dim3(NTHREADS), 0, stream, p);
+        if (!mx && !causal)
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<DD, false, false>), grid, dim3(NTHREADS), 0, stream, p);
+    };
+    if (d == 128)
+        go(std::integral_constant<int, 128>{});
+    else
+        go(std::integral_constant<int, 64>{});
     return hipGetLastError();
 }
 

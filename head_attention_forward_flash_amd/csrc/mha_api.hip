@@ -371,7 +371,7 @@ mha_status fwd_quantised(bool mx, const void* q, mha_strides q_stride, const voi
     const char* name = mx ? "mxfp8" : "fp8";
     mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
     if (st != MHA_OK) return st;
-    if (d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for %s; supported: 128", d, name);
+    if (d != 64 && d != 128) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built for %s; supported: 64 128", d, name);
     const bool has_rows = b > 0 && sq > 0;
     if (has_rows && !q) return fail(MHA_ERR_NULL, "q is NULL");
     if (has_rows && sk > 0 && !k) return fail(MHA_ERR_NULL, "k is NULL");

@@ -199,8 +199,13 @@ hipError_t launch_quant_fp8(const QuantParams& q, const QuantParams& k, const Qu
     const int64_t total = int64_t(q.b) * q.heads * q.nblk + int64_t(k.b) * k.heads * k.nblk +
                           int64_t(v.b) * v.heads * v.nblk;
     if (total == 0) return hipSuccess;
-    if (q.d != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((quant_fp8_kernel<128>), dim3(static_cast<unsigned>(total)), dim3(NT), 0, stream, q, k, v);
+    const dim3 grid(static_cast<unsigned>(total));
+    if (q.d == 128)
+        hipLaunchKernelGGL((quant_fp8_kernel<128>), grid, dim3(NT), 0, stream, q, k, v);
+    else if (q.d == 64)
+        hipLaunchKernelGGL((quant_fp8_kernel<64>), grid, dim3(NT), 0, stream, q, k, v);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

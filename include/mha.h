@@ -202,7 +202,7 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride,
  *   k_mean  [b, hk, d] fp32 contiguous (usually k_smooth_mean's output), or
  *           NULL for no smoothing
  *   o [b, sq, hq, d] bf16 (written); lse [b, hq, sq] fp32 or NULL
- *   d == 128; softmax_scale finite; causal 0 or 1
+ *   d in {64, 128} (the pages time hd128); softmax_scale finite; causal 0 or 1
  *   ws  device workspace of at least mha_fwd_fp8_workspace_bytes(), 256-byte
  *       aligned
  *

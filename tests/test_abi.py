@@ -164,7 +164,7 @@ def test_fp8_refusals_and_layout(lib):
                              a["wsb"], None)
         return st, lib.mha_last_error().decode()
 
-    assert call(d=64)[0] == 3
+    assert call(d=96)[0] == 3
     assert call(v=None)[0] == 1
     assert call(ws=None)[0] == 6
     assert call(wsb=1024)[0] == 6
@@ -192,7 +192,7 @@ def test_mxfp8_refusals_and_layout(lib):
                                a["wsb"], None)
         return st, lib.mha_last_error().decode()
 
-    assert call(d=64)[0] == 3 and "mxfp8" in call(d=64)[1]
+    assert call(d=96)[0] == 3 and "mxfp8" in call(d=96)[1]
     assert call(v=None)[0] == 1
     assert call(ws=None)[0] == 6
     assert call(ws=FAKE + 64)[0] == 6

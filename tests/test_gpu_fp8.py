@@ -61,9 +61,10 @@ def _oracle_mu(k):
     return oracle.k_smooth_mean(k.float().numpy())["mean"].astype(np.float32)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("smooth", [True, False])
-def test_quantised_codes_and_scales_bit_exact(smooth):
-    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 500)
+def test_quantised_codes_and_scales_bit_exact(smooth, d):
+    q, k, v = _inputs(2, 300, 200, 4, 2, d, 500 + d)
     mu = _oracle_mu(k) if smooth else None
     _, _, quant, pad = _fp8_call(q, k, v, mu, causal=False)
     ref_in = {"q": q.float().numpy(), "k": oracle.fp8.smooth_k(k.float().numpy(), mu), "v": v.float().numpy()}
@@ -98,10 +99,11 @@ def _check_attention(q, k, v, mu, causal, what, heads=None, rows=None):
     return rel
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_gqa(causal):
-    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 600)
-    _check_attention(q, k, v, _oracle_mu(k), causal, f"ragged gqa causal={causal}")
+def test_ragged_gqa(causal, d):
+    q, k, v = _inputs(2, 300, 200, 4, 2, d, 600 + d)
+    _check_attention(q, k, v, _oracle_mu(k), causal, f"ragged gqa d{d} causal={causal}")
 
 
 def test_no_smoothing():

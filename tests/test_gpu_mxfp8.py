@@ -57,9 +57,10 @@ def _rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("smooth", [True, False])
-def test_codes_exponents_and_values_bit_exact(smooth):
-    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 5000)
+def test_codes_exponents_and_values_bit_exact(smooth, d):
+    q, k, v = _inputs(2, 300, 200, 4, 2, d, 5000 + d)
     mu = _oracle_mu(k) if smooth else None
     _, _, quant, pads = _call(q, k, v, mu, causal=False)
     qc, qe, _ = oracle.mx_quantize(q.float().numpy())
@@ -94,10 +95,11 @@ def _check(q, k, v, mu, causal, what, heads=None, rows=None):
     assert lerr <= 2.0 ** -6 + 2.0 ** -12 * float(np.abs(lse_ref).max()), f"{what}: LSE max-abs {lerr:.3e}"
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_gqa(causal):
-    q, k, v = _inputs(2, 300, 200, 4, 2, 128, 5100)
-    _check(q, k, v, _oracle_mu(k), causal, f"ragged gqa causal={causal}")
+def test_ragged_gqa(causal, d):
+    q, k, v = _inputs(2, 300, 200, 4, 2, d, 5100 + d)
+    _check(q, k, v, _oracle_mu(k), causal, f"ragged gqa d{d} causal={causal}")
 
 
 def test_no_smoothing_and_negative_scale():

@@ -31,7 +31,8 @@ STATUS_NAMES = {
 
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = (
-    "mha_fwd_bf16", "mha_fwd_bf16_varlen", "mha_fwd_bf16_window_sink", "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
+    "mha_fwd_bf16", "mha_fwd_bf16_varlen", "mha_fwd_bf16_window_sink", "mha_fwd_bf16_varlen_window_sink",
+    "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
     "mha_fwd_mxfp8", "mha_status_string", "mha_last_error",
 )
@@ -69,6 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_fwd_bf16_window_sink.restype = i32
     lib.mha_fwd_bf16_window_sink.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
                                              i32, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp]
+    lib.mha_fwd_bf16_varlen_window_sink.restype = i32
+    lib.mha_fwd_bf16_varlen_window_sink.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp, vp, vp,
+                                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32,
+                                                    vp, vp]
     lib.k_smooth_mean_workspace_bytes.restype = sz
     lib.k_smooth_mean_workspace_bytes.argtypes = [i32] * 6
     lib.k_smooth_mean.restype = i32
@@ -189,12 +194,15 @@ def _thd_strides(t) -> Strides:
 
 
 def mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                        causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse: bool = True):
+                        causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse: bool = True,
+                        window_left: int = -1, window_right: int = -1, sinks=None):
     """Attention forward over packed sequences. q [total_q, hq, d_qk], k/v [total_k, hk, d],
-    cu_seqlens_* int32 [b + 1] on the device. Returns (o [total_q, hq, d_v], lse [hq, total_q] fp32 or None)."""
+    cu_seqlens_* int32 [b + 1] on the device. Returns (o [total_q, hq, d_v], lse [hq, total_q] fp32 or None).
+    A window (-1 = unbounded side) or per-head sinks (fp32 [hq] on the device) select
+    mha_fwd_bf16_varlen_window_sink."""
     torch = _torch()
     lib = load_library()
-    _require_device(q, k, v, out, cu_seqlens_q, cu_seqlens_k)
+    _require_device(q, k, v, out, cu_seqlens_q, cu_seqlens_k, sinks)
     total_q, hq, d_qk = q.shape
     total_k, hk, _ = k.shape
     d_v = v.shape[2]
@@ -204,6 +212,8 @@ def mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
         if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 1-d int32 tensor")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 tensor of hq elements")
     b = cu_seqlens_q.numel() - 1
     if b < 0 or cu_seqlens_k.numel() != b + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold b + 1 offsets")
@@ -212,11 +222,14 @@ def mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     if out is None:
         out = torch.empty((total_q, hq, d_v), dtype=torch.bfloat16, device=q.device)
     lse_t = torch.empty((hq, total_q), dtype=torch.float32, device=q.device) if lse else None
-    _check(lib.mha_fwd_bf16_varlen(_ptr(q), _thd_strides(q), _ptr(k), _thd_strides(k), _ptr(v), _thd_strides(v),
-                                   _ptr(out), _thd_strides(out), _ptr(lse_t), _ptr(cu_seqlens_q),
-                                   _ptr(cu_seqlens_k), b, hq, hk, total_q, total_k, int(max_seqlen_q),
-                                   int(max_seqlen_k), d_qk, d_v, float(softmax_scale), int(bool(causal)),
-                                   _stream(q.device)))
+    args = [_ptr(q), _thd_strides(q), _ptr(k), _thd_strides(k), _ptr(v), _thd_strides(v), _ptr(out),
+            _thd_strides(out), _ptr(lse_t), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, hq, hk, total_q, total_k,
+            int(max_seqlen_q), int(max_seqlen_k), d_qk, d_v, float(softmax_scale), int(bool(causal))]
+    if window_left == -1 and window_right == -1 and sinks is None:
+        _check(lib.mha_fwd_bf16_varlen(*args, _stream(q.device)))
+    else:
+        _check(lib.mha_fwd_bf16_varlen_window_sink(*args, int(window_left), int(window_right), _ptr(sinks),
+                                                   _stream(q.device)))
     return out, lse_t
 
 

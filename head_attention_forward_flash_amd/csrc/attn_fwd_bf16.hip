@@ -89,8 +89,8 @@ template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
 
-// EXT: sliding window (keys j with i - window_left <= j <= i + window_right) and per-head sink
-// logits, for dense (not packed) inputs.
+// EXT: sliding window (keys j with i - window_left <= j <= i + window_right, positions inside
+// the sequence) and per-head sink logits.
 template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
@@ -129,7 +129,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     //      (PAIRED): a workgroup takes block n-1-j and then block j, so every workgroup does
     //      the same work and the grid has no tail of light workgroups.
     static_assert(CAUSAL || !PAIRED, "only causal blocks differ in work");
-    static_assert(!EXT || (!VARLEN && !PAIRED), "windows and sinks run on dense, unpaired grids");
+    static_assert(!EXT || !PAIRED, "windows and sinks run on unpaired grids");
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
@@ -583,9 +583,8 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     // pairing gains 5-10% on 2-8 rounds, nothing on 16).
     const bool ext = p.window_left >= 0 || (!CAUSAL && p.window_right >= 0) || p.sinks != nullptr;
     if (ext) {
-        if (VARLEN) return hipErrorInvalidValue;
         if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, false, true>),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, true>),
                            dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0, stream, p);
         return hipGetLastError();
     }

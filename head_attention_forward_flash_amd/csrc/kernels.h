@@ -30,7 +30,7 @@ struct AttnParams {
     const int* cu_q = nullptr;
     const int* cu_k = nullptr;
     int total_q = 0, total_k = 0;
-    // sliding window (dense inputs only): query i sees keys i - window_left .. i + window_right,
+    // sliding window: query i sees keys i - window_left .. i + window_right (sequence positions),
     // -1 = unbounded on that side; per-query-head sink logits [hq] (nullptr = none)
     int window_left = -1, window_right = -1;
     const float* sinks = nullptr;

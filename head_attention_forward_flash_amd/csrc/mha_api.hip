@@ -194,11 +194,20 @@ mha_status mha_fwd_bf16_window_sink(const void* q, mha_strides q_stride, const v
                     softmax_scale, causal, window_left, window_right, sinks, stream);
 }
 
-mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
-                               const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
-                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int b, int hq, int hk,
-                               int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
-                               float softmax_scale, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mha_status fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
+                           mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int b, int hq, int hk,
+                           int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
+                           float softmax_scale, int causal, int window_left, int window_right, const float* sinks,
+                           void* stream) {
+    if (window_left < -1 || window_right < -1)
+        return fail(MHA_ERR_VALUE, "window_left = %d, window_right = %d: each must be >= -1 (-1 = unbounded)",
+                    window_left, window_right);
+    if (sinks && reinterpret_cast<uintptr_t>(sinks) % 4 != 0) return fail(MHA_ERR_LAYOUT, "sinks must be 4-byte aligned");
     if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(MHA_ERR_SHAPE, "total_q, total_k, max_seqlen_q, max_seqlen_k must be >= 0 (%d %d %d %d)",
                     total_q, total_k, max_seqlen_q, max_seqlen_k);
@@ -250,8 +259,37 @@ mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* 
     p.cu_k = cu_seqlens_k;
     p.total_q = total_q;
     p.total_k = total_k;
+    // a side of the window that reaches past every key of the longest sequence is no bound
+    p.window_left = window_left >= max_seqlen_q ? -1 : window_left;
+    p.window_right = (causal || window_right >= max_seqlen_k) ? -1 : window_right;
+    p.sinks = sinks;
     return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
                       "attn_fwd_bf16 (varlen) launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                               const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int b, int hq, int hk,
+                               int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
+                               float softmax_scale, int causal, void* stream) {
+    return fwd_bf16_varlen(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, cu_seqlens_q, cu_seqlens_k, b, hq,
+                           hk, total_q, total_k, max_seqlen_q, max_seqlen_k, d_qk, d_v, softmax_scale, causal, -1, -1,
+                           nullptr, stream);
+}
+
+mha_status mha_fwd_bf16_varlen_window_sink(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                                           const void* v, mha_strides v_stride, void* o, mha_strides o_stride,
+                                           float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                           int b, int hq, int hk, int total_q, int total_k, int max_seqlen_q,
+                                           int max_seqlen_k, int d_qk, int d_v, float softmax_scale, int causal,
+                                           int window_left, int window_right, const float* sinks, void* stream) {
+    return fwd_bf16_varlen(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, cu_seqlens_q, cu_seqlens_k, b, hq,
+                           hk, total_q, total_k, max_seqlen_q, max_seqlen_k, d_qk, d_v, softmax_scale, causal,
+                           window_left, window_right, sinks, stream);
 }
 
 size_t k_smooth_mean_workspace_bytes(int b, int hk, int sk, int d, int key_stride, int max_keys) {

@@ -6,6 +6,7 @@
  *   mha_fwd_bf16   fused attention forward, bf16 in / bf16 out, fp32 accumulate
  *   mha_fwd_bf16_varlen  the same over packed sequences (cumulative offsets)
  *   mha_fwd_bf16_window_sink  the same with a sliding window and attention sinks
+ *   mha_fwd_bf16_varlen_window_sink  both
  *   k_smooth_mean  per-(batch, kv head) K mean behind a gate (two kernels, one call)
  *   mha_fwd_fp8    K-smoothed FP8 (E4M3) block-quantised attention forward
  *   mha_fwd_mxfp8  the same with MXFP8 (E8M0 exponent per 32 channels) quantisation
@@ -159,6 +160,25 @@ mha_status mha_fwd_bf16_varlen(const void* q, mha_strides q_stride,
                                int b, int hq, int hk, int total_q, int total_k,
                                int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
                                float softmax_scale, int causal, void* stream);
+
+/*
+ * mha_fwd_bf16_varlen_window_sink - mha_fwd_bf16_varlen with the sliding window
+ * and per-head sinks of mha_fwd_bf16_window_sink (the GPT-OSS shapes are
+ * served packed): window positions are counted inside each sequence, sinks
+ * is a [hq] fp32 device array or NULL.  Arguments, layouts and errors as the
+ * two calls it combines.
+ */
+mha_status mha_fwd_bf16_varlen_window_sink(const void* q, mha_strides q_stride,
+                                           const void* k, mha_strides k_stride,
+                                           const void* v, mha_strides v_stride,
+                                           void* o, mha_strides o_stride,
+                                           float* lse,
+                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                           int b, int hq, int hk, int total_q, int total_k,
+                                           int max_seqlen_q, int max_seqlen_k, int d_qk, int d_v,
+                                           float softmax_scale, int causal,
+                                           int window_left, int window_right, const float* sinks,
+                                           void* stream);
 
 /*
  * k_smooth_mean - the K-smoothing gate of "[HIP] Mha v4: run the K-smoothing

@@ -51,4 +51,4 @@ from .fp8 import (  # noqa: F401
     fp8_attention_forward,
 )
 from .mx import mx_quantize, mx_dequantize, mxfp8_attention_forward  # noqa: F401
-from .window import attention_window_sink, visible_mask, visible_pairs  # noqa: F401
+from .window import attention_window_sink, attention_varlen_window_sink, visible_mask, visible_pairs  # noqa: F401

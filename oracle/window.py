@@ -85,3 +85,34 @@ def attention_window_sink(q, k, v, *, scale, causal, window_left=-1, window_righ
             o[bi, :, hi, :] = out
             lse[bi, hi, :] = np.where(alive, m_safe + np.log(np.where(alive, denom, 1.0)), -np.inf)
     return o, lse
+
+
+def attention_varlen_window_sink(q, k, v, cu_q, cu_k, *, scale, causal, window_left=-1, window_right=-1,
+                                 sinks=None, heads=None, rows=None):
+    """``attention_window_sink`` over packed sequences (THD tensors, b + 1 offsets per axis): each
+    sequence attends to its own keys, window positions counted inside the sequence.
+
+    Returns (o [nrows, nheads, d_v], lse [nheads, nrows]), both float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    total_q, hq, _ = q.shape
+    d_v = v.shape[2]
+    heads = list(range(hq)) if heads is None else list(heads)
+    rows = list(range(total_q)) if rows is None else list(rows)
+    o = np.zeros((len(rows), len(heads), d_v), dtype=np.float64)
+    lse = np.full((len(heads), len(rows)), -np.inf, dtype=np.float64)
+    for i in range(len(cu_q) - 1):
+        qa, qe, ka, ke = cu_q[i], cu_q[i + 1], cu_k[i], cu_k[i + 1]
+        sel = [n for n, r in enumerate(rows) if qa <= r < qe]
+        if not sel:
+            continue
+        oi, li = attention_window_sink(q[None, qa:qe], k[None, ka:ke], v[None, ka:ke], scale=scale, causal=causal,
+                                       window_left=window_left, window_right=window_right, sinks=sinks,
+                                       heads=heads, rows=[rows[n] - qa for n in sel])
+        o[sel] = oi[0]
+        lse[:, sel] = li[0]
+    return o, lse

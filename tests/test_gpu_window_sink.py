@@ -124,3 +124,27 @@ def test_gptoss_full_sink_workload_sampled():
     sinks = workloads.make_sinks(w).numpy()
     rows = workloads.sample_indices(w.sq, 96, 22, include=[0, 1, w.sq - 1])
     _check(q, k, v, w.causal, -1, -1, sinks, "gpt-oss full layer", rows=rows, heads=[5, 40])
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)], ids=["d64", "d128"])
+@pytest.mark.parametrize("causal,left,right", [(True, 127, -1), (False, 40, 25)])
+def test_packed_sequences_with_window_and_sinks(dims, causal, left, right):
+    # positions restart per sequence; lengths below, at and above the 128-row blocks
+    import head_attention_forward_flash_amd as mha
+    dev = require_gpu()
+    dqk, dv = dims
+    lens = [1, 300, 129, 77, 128]
+    q = workloads.make_random((sum(lens), 4, dqk), 6600 + dqk)
+    k = workloads.make_random((sum(lens), 2, dqk), 6601 + dqk)
+    v = workloads.make_random((sum(lens), 2, dv), 6602 + dqk)
+    sinks = np.array([0.3, -2.0, 1.5, 0.0], dtype=np.float32)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    o, lse = mha.mha_fwd_bf16_varlen(q.to(dev), k.to(dev), v.to(dev), cu, cu, max(lens), max(lens), causal=causal,
+                                     window_left=left, window_right=right, sinks=torch.from_numpy(sinks).to(dev))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen_window_sink(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                                       cu.cpu().numpy(), cu.cpu().numpy(), scale=dqk ** -0.5,
+                                                       causal=causal, window_left=left, window_right=right,
+                                                       sinks=sinks.astype(np.float64))
+    assert_bf16_parity(to_np(o.cpu()), o_ref, lse.cpu().numpy().astype(np.float64), l_ref,
+                       f"packed window d{dqk} causal={causal} ({left},{right})")

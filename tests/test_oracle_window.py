@@ -144,3 +144,36 @@ def test_visible_pairs():
     assert W.visible_pairs(10, 10, causal=True) == 55
     assert W.visible_pairs(10, 10, causal=True, window_left=2) == 1 + 2 + 3 * 8
     assert W.visible_pairs(6, 6, causal=False, window_left=1, window_right=1) == 2 + 3 * 4 + 2
+
+
+def test_packed_sequences_without_window_are_plain_varlen():
+    lens_q, lens_k = [5, 1, 9, 0], [7, 3, 9, 2]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    q = RNG.standard_normal((sum(lens_q), 4, 6))
+    k = RNG.standard_normal((sum(lens_k), 2, 6))
+    v = RNG.standard_normal((sum(lens_k), 2, 3))
+    for causal in (False, True):
+        o, lse = W.attention_varlen_window_sink(q, k, v, cu_q, cu_k, scale=0.4, causal=causal)
+        o_r, lse_r = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=0.4, causal=causal)
+        np.testing.assert_array_equal(o, o_r)
+        np.testing.assert_array_equal(lse, lse_r)
+
+
+def test_packed_sequences_match_each_sequence_alone():
+    # positions restart in every sequence: sequence 1 alone, as a dense batch of one, gives the
+    # same rows as its slice of the packed call
+    lens = [6, 11, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = RNG.standard_normal((sum(lens), 2, 5))
+    k = RNG.standard_normal((sum(lens), 1, 5))
+    v = RNG.standard_normal((sum(lens), 1, 4))
+    sinks = np.array([0.7, -0.2])
+    o, lse = W.attention_varlen_window_sink(q, k, v, cu, cu, scale=0.5, causal=True, window_left=2, sinks=sinks)
+    a, e = cu[1], cu[2]
+    o1, l1 = W.attention_window_sink(q[None, a:e], k[None, a:e], v[None, a:e], scale=0.5, causal=True,
+                                     window_left=2, sinks=sinks)
+    np.testing.assert_array_equal(o[a:e], o1[0])
+    np.testing.assert_array_equal(lse[:, a:e], l1[0])
+    # a window of 2 in the packed axis would reach into sequence 0; per sequence it cannot
+    assert not np.allclose(o[a], W.attention_window_sink(q[None], k[None], v[None], scale=0.5, causal=True,
+                                                         window_left=2, sinks=sinks)[0][0, a])

@@ -512,16 +512,43 @@ next_item:
             qk_block(k_slot(Zero{}), 0, s);
             if (need_mask(2 * t0)) mask_block(2 * t0, s);
             float mx = lane_max(s);
+            // Tiles up to `need` hold a key that some row of this wave sees; past them (the
+            // diagonal tiles of the rows above, or right of a window) the wave only keeps the
+            // ring's waits, barriers and its share of the DMA.  Wave-uniform.
+            int need = ntiles;
+            if constexpr (CAUSAL) need = min(ntiles, (wave_row0 + 31) / BN + 1);
+            if constexpr (EXT && !CAUSAL) {
+                if (p.window_right >= 0) need = min(ntiles, (wave_row0 + 31 + p.window_right) / BN + 1);
+            }
+            const int e = min(need, ntiles - 1);   // tiles run through iteration()
             int t = t0;
-            for (; t + 2 < ntiles; t += 2) {
+            for (; t + 2 <= e; t += 2) {
                 iteration(t, Zero{}, s, mx);
                 iteration(t + 1, One{}, s, mx);
             }
-            if (t + 1 < ntiles) {
-                iteration(t, Zero{}, s, mx);
-                last(t + 1, One{}, s, mx);
+            const bool odd = t < e;
+            if (odd) iteration(t++, Zero{}, s, mx);
+            if (need == ntiles) {
+                if (odd) last(t, One{}, s, mx);
+                else last(t, Zero{}, s, mx);
             } else {
-                last(t, Zero{}, s, mx);
+                // tile t has parity (t - t0) & 1; the last tile issues no further DMA
+                auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {
+                    using Cur = std::integral_constant<int, decltype(par_c)::value>;
+                    using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+                    __syncthreads();
+                    if (u + 1 < ntiles) {
+                        issue_k(u + 2, k_slot(Cur{}));
+                        issue_v(u + 1, v_slot(Nxt{}));
+                    }
+                };
+                bool par = odd;
+                for (; t < ntiles; ++t) {
+                    if (par) drain(t, One{});
+                    else drain(t, Zero{});
+                    par = !par;
+                }
             }
         }
 

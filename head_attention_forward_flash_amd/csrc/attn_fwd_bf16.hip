@@ -572,16 +572,7 @@ next_item:
         const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
         if (my_row < sq) {
             uint16_t* orow = static_cast<uint16_t*>(p.o) + (orow0 + h * p.ov.sh + my_row * p.ov.ss);
-#pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) {
-#pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    const int ch = cb * 32 + grp * 8 + half * 4;
-                    const uint32_t w0 = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
-                    const uint32_t w1 = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + ch) = u32x2{w0, w1};
-                }
-            }
+            store_o_row<CBLK>(orow, oacc, inv, half);
             if (p.lse != nullptr && half == 0) {
                 const float lse = l_tot > 0.f ? (m_log2 + __log2f(l_tot)) * kLn2 : kNegInf;
                 p.lse[lse0 + my_row] = lse;

@@ -481,16 +481,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (my_row < p.sq) {
         uint16_t* orow = static_cast<uint16_t*>(p.o) + (bb * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss);
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int ch = cb * 32 + grp * 8 + half * 4;
-                const uint32_t w0 = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
-                const uint32_t w1 = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + ch) = u32x2{w0, w1};
-            }
-        }
+        store_o_row<CBLK>(orow, oacc, inv, half);
         if (p.lse != nullptr && half == 0) {
             const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;   // m_run is scaled
             p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;

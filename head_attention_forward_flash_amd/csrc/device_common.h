@@ -90,6 +90,37 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// The O^T accumulators of one lane (one output row; in each 8-channel group the lane holds 4
+// channels and lane ^ 32 the other 4), scaled by inv and rounded to bf16, stored to that row:
+// lanes l and l + 32 trade one 4-channel half per pair of groups, so that every lane stores 16
+// contiguous bytes (half the store instructions of 8-byte pieces).  Both lanes of a pair must
+// be active.
+template <int CBLK>
+__device__ __forceinline__ void store_o_row(uint16_t* orow, const f32x16 (&oacc)[CBLK], float inv, int half) {
+    auto swp = [](uint32_t x) __attribute__((always_inline)) {
+        return __builtin_bit_cast(uint32_t, swap_halves(__builtin_bit_cast(float, x)));
+    };
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            uint32_t w[2][2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int grp = 2 * gp + k;
+                w[k][0] = pack_bf16x2(oacc[cb][grp * 4 + 0] * inv, oacc[cb][grp * 4 + 1] * inv);
+                w[k][1] = pack_bf16x2(oacc[cb][grp * 4 + 2] * inv, oacc[cb][grp * 4 + 3] * inv);
+            }
+            // half 0 keeps group 2gp and takes its partner's half of it; half 1 keeps 2gp + 1
+            const uint32_t r0 = swp(half ? w[0][0] : w[1][0]);
+            const uint32_t r1 = swp(half ? w[0][1] : w[1][1]);
+            const int ch = cb * 32 + (2 * gp + half) * 8;
+            *reinterpret_cast<u32x4*>(orow + ch) =
+                half ? u32x4{r0, r1, w[1][0], w[1][1]} : u32x4{w[0][0], w[0][1], r0, r1};
+        }
+    }
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
 // acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 against (1, 1)).

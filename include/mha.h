@@ -20,9 +20,10 @@
  *   non-negative.
  *
  *   All tensor pointers are DEVICE pointers owned by the caller.  The library
- *   allocates no device memory and keeps no state between calls; where a call
- *   needs scratch space the caller passes a workspace whose size is given by
- *   the matching *_workspace_bytes() query.
+ *   allocates no device memory and keeps no state between calls other than a
+ *   host-side cache of each kernel's occupancy per device (used to size grids);
+ *   where a call needs scratch space the caller passes a workspace whose size
+ *   is given by the matching *_workspace_bytes() query.
  *
  *   `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Calls return after enqueueing; nothing synchronises.  Kernel faults

@@ -195,8 +195,8 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(attention heads shard across GPUs with no communication; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (attention heads shard "
+              "across GPUs without communication, so one GPU's share of the heads is the measured unit).",
               file=sys.stderr)
         sys.exit(2)
 

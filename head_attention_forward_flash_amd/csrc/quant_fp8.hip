@@ -9,8 +9,9 @@
 //   x      = fp32(bf16 input)                 (K: fp32(K) - mean[b, h, c], one fp32 rounding)
 //   amax   = max |x| over the block's tokens and channels (wave max, then LDS)
 //   scale  = amax / 448 in fp32 (1 when amax == 0)
-//   code   = E4M3(x / scale): IEEE fp32 division, clamp to +-448 (a no-op except
-//            for the last half-ulp above 448, which rounds to 448 anyway), then
+//   code   = E4M3(x / scale): the correctly rounded fp32 quotient (one reciprocal per
+//            thread and a corrected product per element), clamp to +-448 (a no-op
+//            except for the last half-ulp above 448, which rounds to 448 anyway), then
 //            v_cvt_pk_fp8_f32 (round to nearest even)
 // Codes go to a token-padded [b, h, nblk*128, D] array (tokens past s are
 // written as zero codes), scales to [b, h, nblk].  For V the codes' values are
@@ -142,7 +143,35 @@ __device__ __forceinline__ void quant_block(const QuantParams& p, int id, float*
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float scale = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax > 0.f ? amax / 448.0f : 1.0f)));
+
+    // x / scale, correctly rounded, without a full division per element: with y = RN(1/scale),
+    // q = RN(x y) is within an ulp of the quotient, r = x - q scale is exact in one FMA, and
+    // RN(q + r y) is the correctly rounded quotient (Markstein's correction step; P. Markstein,
+    // "IA-64 and Elementary Functions", the division theorems of its chapter on division).
+    // r stays exact while |x| >= 2^-102; below that, with scale >= 2^-90, both quotients are
+    // under 2^-12 and encode to the same (zero) code, their sign taken from x.  Blocks with a
+    // smaller scale divide element by element.
+    if (scale >= 0x1p-90f) {
+        const float recip = 1.0f / scale;
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = x[ps][i];
+                const float q = v * recip;
+                const float r = fmaf(-q, scale, v);
+                x[ps][i] = copysignf(fmaf(r, recip, q), v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[ps][i] = x[ps][i] / scale;
+        }
+    }
 
     const int64_t elem0 = static_cast<int64_t>(bh) * p.nblk * TOK + blk * TOK;   // first row of the block
 #pragma unroll
@@ -152,7 +181,7 @@ __device__ __forceinline__ void quant_block(const QuantParams& p, int id, float*
         for (int half = 0; half < 2; ++half) {
             float y[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[ps][half * 4 + j] / scale, -448.f), 448.f);
+            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[ps][half * 4 + j], -448.f), 448.f);
             int wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
             wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wv, true);
             packed[half] = static_cast<uint32_t>(wv);

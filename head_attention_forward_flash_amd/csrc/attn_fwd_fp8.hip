@@ -186,7 +186,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         } else {
             const int kblk = min((t * BN) / BM, p.nk - 1);   // past the last tile: any valid block
             const float sv = v_scale[kblk];
-            return TileScale{fmaxf(cq * k_scale[kblk], kMinFactor), __log2f(sv), 1.f / sv};
+            // 1/sv only rescales the row sum: the hardware reciprocal (1 ulp) is enough
+            return TileScale{fmaxf(cq * k_scale[kblk], kMinFactor), __log2f(sv), __builtin_amdgcn_rcpf(sv)};
         }
     };
 
@@ -415,14 +416,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         issue_k(t + 2, k_slot(Cur{}));
         issue_v(t + 1, v_slot(Nxt{}));
         mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{});
-        s = sn;
-        // block 2t+1 with block 2t+2 (the first block of the next tile)
+        // block 2t+1 (now in sn) with block 2t+2 (the first block of the next tile), whose S goes
+        // into s: the two score buffers swap roles instead of being copied
         bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Nxt{}), 0, ke[1][0], sn, s, sc.c, bias, pf);
-        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
+        region_a(k_slot(Nxt{}), 0, ke[1][0], s, sn, sc.c, bias, pf);
+        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, s);
         __builtin_amdgcn_sched_barrier(0);
-        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, sn, sc_next.c, NoVmem{});
-        s = sn;
+        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, s, sc_next.c, NoVmem{});
         sc = sc_next;
         ke[0] = ke[1];
         ke[1] = ke_new;

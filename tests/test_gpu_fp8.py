@@ -77,6 +77,26 @@ def test_quantised_codes_and_scales_bit_exact(smooth, d):
     assert (pad["q"] == 0).all() and (pad["k"] == 0).all(), "token padding must be zero codes"
 
 
+def test_quantised_codes_bit_exact_at_tiny_magnitudes():
+    # Heads scaled by powers of two (exact in bf16) move the block scales across the
+    # quantiser's two division paths: the corrected reciprocal product for scales of at least
+    # 2^-90 (head 1: scales near 2^-87, with elements small enough for the residual to
+    # underflow) and the plain division below (head 2: scales near 2^-107).  Head 0 is the
+    # usual N(0, 1) case.  Codes and scales must match the oracle's IEEE quotient bit for bit.
+    q, k, v = _inputs(1, 260, 260, 3, 3, 128, 540, bias_std=0.0)
+    factors = torch.tensor([1.0, 2.0 ** -80, 2.0 ** -100])
+    q, k, v = (t.float() * factors[None, None, :, None] for t in (q, k, v))
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    _, _, quant, _ = _fp8_call(q, k, v, None, causal=False)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        codes_ref, scales_ref, _ = oracle.quantize_blocks(x.float().numpy())
+        codes_gpu, scales_gpu = quant[name]
+        assert scales_ref[0, 1].max() >= 2.0 ** -90 > scales_ref[0, 2].max(), "inputs must span both paths"
+        np.testing.assert_array_equal(scales_gpu, scales_ref, err_msg=f"{name} scales")
+        mism = int((codes_gpu != codes_ref).sum())
+        assert mism == 0, f"{name}: {mism} of {codes_ref.size} E4M3 codes differ"
+
+
 def _check_attention(q, k, v, mu, causal, what, heads=None, rows=None):
     o, lse, _, _ = _fp8_call(q, k, v, mu, causal)
     d = q.shape[3]

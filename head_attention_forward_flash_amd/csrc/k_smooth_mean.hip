@@ -124,8 +124,8 @@ __global__ __launch_bounds__(NT) void k_fold_gate_kernel(const GateParams p) {
     if (tid < D && p.n_samples > 0) {
         const float* src = p.partial + static_cast<int64_t>(bh) * p.n_chunks * 2 * D;
         float a = 0.f, b2 = 0.f;
-        // ascending chunk order; eight chunks' partials are loaded before they are added
-        constexpr int FOLD = 8;
+        // ascending chunk order; sixteen chunks' partials are loaded before they are added
+        constexpr int FOLD = 16;
         for (int c0 = 0; c0 < p.n_chunks; c0 += FOLD) {
             float pa[FOLD], pb[FOLD];
 #pragma unroll
@@ -148,14 +148,29 @@ __global__ __launch_bounds__(NT) void k_fold_gate_kernel(const GateParams p) {
     num[tid] = tid < D ? mu * mu : 0.f;
     den[tid] = tid < D ? var : 0.f;
     __syncthreads();
-    for (int w = NT / 2; w > 0; w >>= 1) {
-        if (tid < w) {
-            num[tid] += num[tid + w];
-            den[tid] += den[tid + w];
+    // Pairwise tree over the NT slots: at level w, slot t < w adds slot t + w.  Levels whose
+    // upper half lies past the D channels only add zeros and are skipped; levels w >= 64 pair
+    // slots of different waves and go through LDS, the last six run inside each wave with lane
+    // shuffles in the same pairing (every wave computes the same totals, so none has to wait
+    // for another's).
+#pragma unroll
+    for (int w = NT / 2; w >= 64; w >>= 1) {
+        if (w < D) {
+            if (tid < w) {
+                num[tid] += num[tid + w];
+                den[tid] += den[tid + w];
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
-    const float sn = num[0], sd = den[0];
+    float sn = num[tid & 63], sd = den[tid & 63];
+#pragma unroll
+    for (int w = 32; w > 0; w >>= 1) {
+        sn += __shfl_down(sn, w, 64);
+        sd += __shfl_down(sd, w, 64);
+    }
+    sn = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sn)));
+    sd = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sd)));
     float r;
     if (sd > 0.f) r = sqrtf(sn / sd);
     else r = sn > 0.f ? __builtin_inff() : 0.f;

@@ -294,6 +294,7 @@ next_item:
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
         float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
         float l_run = 0.f;       // this lane's partial row sum over its half of the keys
+        float mc_run = 0.f;      // m_run * c, or 0 while m_run = -inf
 
         // fragment addresses inside a slot (bytes)
         const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
@@ -311,13 +312,26 @@ next_item:
 #pragma unroll
         for (int j = 0; j < KSW / 2; ++j) koff[j] = col * KROWB + ((2 * j + half) ^ kx) * 16;
 
+        // ---- K fragment of k-step kk of the 32-key block kb of a K tile
+        auto k_frag = [&](const uint8_t* kl, int kb, int kk) __attribute__((always_inline)) {
+            const uint8_t* a_ptr = kl + koff[kk % (KSW / 2)] + (kk / (KSW / 2)) * KSW * 16 + kb * 32 * KROWB;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_ptr));
+        };
+        // The first KPRE fragments of a block's S are read ahead, at the end of the region before
+        // the one that multiplies them, so the S MFMAs never start on an LDS read just issued.
+        constexpr int KPRE = KSTEPS < 2 ? KSTEPS : 2;
+        static_assert(KPRE <= KSTEPS, "prefetch at most one block's fragments");
+        using KPre = bf16x8[KPRE];
+        auto k_prefetch = [&](const uint8_t* kl, int kb, KPre& pre) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kk = 0; kk < KPRE; ++kk) pre[kk] = k_frag(kl, kb, kk);
+        };
         // ---- S^T = K Q^T for the 32-key block kb of a K tile (one accumulator)
-        auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s) __attribute__((always_inline)) {
+        auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s, const KPre& pre) __attribute__((always_inline)) {
             s = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
-                const uint8_t* a_ptr = kl + koff[kk % (KSW / 2)] + (kk / (KSW / 2)) * KSW * 16 + kb * 32 * KROWB;
-                const auto a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_ptr));
+                const auto a = kk < KPRE ? pre[kk] : k_frag(kl, kb, kk);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
             }
         };
@@ -356,18 +370,24 @@ next_item:
         };
         // ---- online softmax update from a block max (the reference max only moves when a row's
         //      max grows by more than 2^8 in probability); returns m * c for the exponentials
+        //      A row grows when (block max - m_run) * c exceeds the threshold: a first finite max
+        //      (m_run = -inf) gives +inf, and a row that has seen no key yet (-inf - -inf) gives
+        //      NaN, which compares false.  mc_run = m_run * c (0 while m_run = -inf) changes only
+        //      here, so the common path is one exchange, one max, a subtract, a multiply, a compare
+        //      and a branch.
         auto softmax_update = [&](float mx) __attribute__((always_inline)) {
             const float mt = fmaxf(mx, swap_halves(mx));
-            const float m_new = fmaxf(m_run, mt);
-            const bool grow = m_new > m_run && (m_run == kNegInf || (m_new - m_run) * c > kRescaleThreshold);
+            const bool grow = (mt - m_run) * c > kRescaleThreshold;
             if (__any(grow)) {
+                const float m_new = fmaxf(m_run, mt);
                 const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
                 l_run *= alpha;
 #pragma unroll
                 for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
                 m_run = m_new;
+                mc_run = m_new == kNegInf ? 0.f : m_new * c;
             }
-            return m_run == kNegInf ? 0.f : m_run * c;
+            return mc_run;
         };
         // ---- P^T = exp2(S^T c - m c) rounded to bf16, as the B operands of two 16-key P.V steps
         auto exp_block = [&](const f32x16& s, float mc, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
@@ -427,23 +447,30 @@ next_item:
         // region A: S of the next block (KSTEPS MFMAs, one K read each) under the exponentials
         //           of the current block
         auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float mc,
-                            bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+                            bf16x8 (&pf)[2], const KPre& pre) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
-            qk_block(kl, kb, sn);
+            qk_block(kl, kb, sn, pre);
             exp_block(s, mc, pf);
             // keep the exponentials here: without a use inside the region the compiler would sink
             // them to the P.V MFMAs that consume them
             asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-            sched_region<KSTEPS, KSTEPS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
+            sched_region<KSTEPS, KSTEPS - KPRE, 0, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
             __builtin_amdgcn_sched_barrier(0);
         };
-        // region B: P.V of the current block under its row sum and the next block's lane max
+        // region B: P.V of the current block under its row sum and the next block's lane max;
+        // with PRE, it also reads the first fragments of the next region A's K block
         auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], const f32x16& sn,
-                            auto vmem_c) __attribute__((always_inline)) {
+                            auto vmem_c, auto pre_c, const uint8_t* kl_next, int kb_next,
+                            KPre& pre) __attribute__((always_inline)) {
+            constexpr int NPRE = decltype(pre_c)::value ? KPRE : 0;
             pv_block(vl, kb, pf);
             row_sum(pf);
             const float mx = lane_max(sn);
-            sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+            if constexpr (NPRE > 0) k_prefetch(kl_next, kb_next, pre);
+            // keep the row sum here: without a use inside the region the compiler would sink it
+            // past the region's end, where nothing hides it
+            asm volatile("" ::"v"(l_run));
+            sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
                 std::make_integer_sequence<int, PV_MFMA>{});
             __builtin_amdgcn_sched_barrier(0);
             return mx;
@@ -458,42 +485,45 @@ next_item:
         using NoVmem = std::integral_constant<int, 0>;
         using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
         // a tile that is not the last: its two blocks and the S of the next tile's first block
-        auto iteration = [&](int t, auto par_c, f32x16& s, float& mx) __attribute__((always_inline)) {
+        using Pre = std::true_type;
+        using NoPre = std::false_type;
+        auto iteration = [&](int t, auto par_c, f32x16& s, float& mx, KPre& pre) __attribute__((always_inline)) {
             using Cur = std::integral_constant<int, decltype(par_c)::value>;
             using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
             f32x16 sn;
             bf16x8 pf[2];
             // block 2t (exponentials, P.V) with block 2t+1 (S, max)
             float mc = softmax_update(mx);
-            region_a(k_slot(Cur{}), 1, sn, s, mc, pf);
+            region_a(k_slot(Cur{}), 1, sn, s, mc, pf, pre);
             if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
             __builtin_amdgcn_s_waitcnt(WAIT_VM0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
             issue_k(t + 2, k_slot(Cur{}));
             issue_v(t + 1, v_slot(Nxt{}));
-            mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{});
+            mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
             s = sn;
             // block 2t+1 with block 2t+2 (the first block of the next tile)
             mc = softmax_update(mx);
-            region_a(k_slot(Nxt{}), 0, sn, s, mc, pf);
+            region_a(k_slot(Nxt{}), 0, sn, s, mc, pf, pre);
             if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
             __builtin_amdgcn_sched_barrier(0);
-            mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{});
+            // the next region A (an iteration or the last tile) starts on block 1 of K_{t+1}
+            mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
             s = sn;
         };
         // the last tile: its two blocks, nothing further to load
-        auto last = [&](int t, auto par_c, const f32x16& s0, float mx) __attribute__((always_inline)) {
+        auto last = [&](int t, auto par_c, const f32x16& s0, float mx, KPre& pre) __attribute__((always_inline)) {
             using Cur = std::integral_constant<int, decltype(par_c)::value>;
             f32x16 sn;
             bf16x8 pf[2];
             float mc = softmax_update(mx);
-            region_a(k_slot(Cur{}), 1, sn, s0, mc, pf);
+            region_a(k_slot(Cur{}), 1, sn, s0, mc, pf, pre);
             if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
             __builtin_amdgcn_s_waitcnt(WAIT_VM0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{});
+            mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{}, NoPre{}, nullptr, 0, pre);
             mc = softmax_update(mx);
             exp_block(sn, mc, pf);
             row_sum(pf);
@@ -509,9 +539,12 @@ next_item:
             __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_t0 has landed
             __syncthreads();
             f32x16 s;
-            qk_block(k_slot(Zero{}), 0, s);
+            KPre pre;
+            k_prefetch(k_slot(Zero{}), 0, pre);
+            qk_block(k_slot(Zero{}), 0, s, pre);
             if (need_mask(2 * t0)) mask_block(2 * t0, s);
             float mx = lane_max(s);
+            k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_t0
             // Tiles up to `need` hold a key that some row of this wave sees; past them (the
             // diagonal tiles of the rows above, or right of a window) the wave only keeps the
             // ring's waits, barriers and its share of the DMA.  Wave-uniform.
@@ -523,14 +556,14 @@ next_item:
             const int e = min(need, ntiles - 1);   // tiles run through iteration()
             int t = t0;
             for (; t + 2 <= e; t += 2) {
-                iteration(t, Zero{}, s, mx);
-                iteration(t + 1, One{}, s, mx);
+                iteration(t, Zero{}, s, mx, pre);
+                iteration(t + 1, One{}, s, mx, pre);
             }
             const bool odd = t < e;
-            if (odd) iteration(t++, Zero{}, s, mx);
+            if (odd) iteration(t++, Zero{}, s, mx, pre);
             if (need == ntiles) {
-                if (odd) last(t, One{}, s, mx);
-                else last(t, Zero{}, s, mx);
+                if (odd) last(t, One{}, s, mx, pre);
+                else last(t, Zero{}, s, mx, pre);
             } else {
                 // tile t has parity (t - t0) & 1; the last tile issues no further DMA
                 auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {

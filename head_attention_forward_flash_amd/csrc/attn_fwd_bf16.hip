@@ -359,13 +359,16 @@ next_item:
             }
         };
         // ---- this lane's max over its 16 scores of a block
+        //      (three-operand maxima only: a two-operand maximum of scores that may come from the
+        //      mask's select costs two extra canonicalising instructions)
         auto lane_max = [&](const f32x16& s) __attribute__((always_inline)) {
-            float a = __builtin_fmaxf(s[0], s[1]);
-            float b = __builtin_fmaxf(s[14], s[15]);
-#pragma unroll
-            for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
-#pragma unroll
-            for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
+            float a = max3(s[0], s[1], s[2]);
+            float b = max3(s[8], s[9], s[10]);
+            a = max3(a, s[3], s[4]);
+            b = max3(b, s[11], s[12]);
+            a = max3(a, s[5], s[6]);
+            b = max3(b, s[13], s[14]);
+            a = max3(a, s[7], s[15]);
             return __builtin_fmaxf(a, b);
         };
         // ---- online softmax update from a block max (the reference max only moves when a row's
@@ -373,13 +376,12 @@ next_item:
         //      A row grows when (block max - m_run) * c exceeds the threshold: a first finite max
         //      (m_run = -inf) gives +inf, and a row that has seen no key yet (-inf - -inf) gives
         //      NaN, which compares false.  mc_run = m_run * c (0 while m_run = -inf) changes only
-        //      here, so the common path is one exchange, one max, a subtract, a multiply, a compare
-        //      and a branch.
+        //      here, so the common path is one exchange, one three-operand max, a subtract, a
+        //      multiply, a compare and a branch.
         auto softmax_update = [&](float mx) __attribute__((always_inline)) {
-            const float mt = fmaxf(mx, swap_halves(mx));
-            const bool grow = (mt - m_run) * c > kRescaleThreshold;
+            const float m_new = max_with_partner(mx, m_run);
+            const bool grow = (m_new - m_run) * c > kRescaleThreshold;
             if (__any(grow)) {
-                const float m_new = fmaxf(m_run, mt);
                 const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
                 l_run *= alpha;
 #pragma unroll
@@ -405,14 +407,12 @@ next_item:
         };
         // ---- row sum of the rounded P fed to P.V
         auto row_sum = [&](const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-            float a = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+                for (int i = 0; i < 4; ++i) l_run = add_bf16_pair(w[i], l_run);
             }
-            l_run += a;
         };
         // ---- O^T += V^T P^T over the 32-key block kb of a V tile: the A operand (32 channels x
         //      16 keys) comes from two transposing reads of row-major V; keys ks*16 +

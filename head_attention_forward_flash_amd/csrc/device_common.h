@@ -90,6 +90,19 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// max(x of this lane, x of lane ^ 32, y).  v_permlane32_swap on two copies of x leaves the lower
+// half's x in one register and the upper half's in the other on every lane, so one v_max3 takes
+// the maximum without a lane select.  Written as one asm block: the builtin's second result is
+// miscompiled by this compiler when it is not consumed through a lane select.  The s_nop 1 gives
+// the two wait states a VALU write needs before v_permlane32_swap reads it.
+__device__ __forceinline__ float max_with_partner(float x, float y) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max3_f32 %0, %0, %1, %2"
+                 : "+v"(a), "+v"(b)
+                 : "v"(y));
+    return a;
+}
+
 // The O^T accumulators of one lane (one output row; in each 8-channel group the lane holds 4
 // channels and lane ^ 32 the other 4), scaled by inv and rounded to bf16, stored to that row:
 // lanes l and l + 32 trade one 4-channel half per pair of groups, so that every lane stores 16

@@ -295,6 +295,7 @@ next_item:
         float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
         float l_run = 0.f;       // this lane's partial row sum over its half of the keys
         float mc_run = 0.f;      // m_run * c, or 0 while m_run = -inf
+        float grow_at = kNegInf; // mc_run + threshold, or -inf while m_run = -inf
 
         // fragment addresses inside a slot (bytes)
         const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
@@ -373,14 +374,14 @@ next_item:
         };
         // ---- online softmax update from a block max (the reference max only moves when a row's
         //      max grows by more than 2^8 in probability); returns m * c for the exponentials
-        //      A row grows when (block max - m_run) * c exceeds the threshold: a first finite max
-        //      (m_run = -inf) gives +inf, and a row that has seen no key yet (-inf - -inf) gives
-        //      NaN, which compares false.  mc_run = m_run * c (0 while m_run = -inf) changes only
-        //      here, so the common path is one exchange, one three-operand max, a subtract, a
-        //      multiply, a compare and a branch.
+        //      A row grows when m_new * c exceeds grow_at = m_run * c + threshold; while m_run is
+        //      -inf, grow_at is -inf, so a first finite max always grows and a row that has seen
+        //      no key yet (m_new = -inf) does not.  mc_run and grow_at change only on growth, so
+        //      the common path is one exchange, one three-operand max, a multiply, a compare and
+        //      a branch.
         auto softmax_update = [&](float mx) __attribute__((always_inline)) {
             const float m_new = max_with_partner(mx, m_run);
-            const bool grow = (m_new - m_run) * c > kRescaleThreshold;
+            const bool grow = m_new * c > grow_at;
             if (__any(grow)) {
                 const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
                 l_run *= alpha;
@@ -388,6 +389,7 @@ next_item:
                 for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
                 m_run = m_new;
                 mc_run = m_new == kNegInf ? 0.f : m_new * c;
+                grow_at = m_new == kNegInf ? kNegInf : mc_run + kRescaleThreshold;
             }
             return mc_run;
         };

@@ -45,6 +45,13 @@
 namespace mha {
 namespace {
 
+// max(x of this lane, x of lane ^ 32): the exchange of max_with_partner followed by one v_max.
+__device__ __forceinline__ float max_halves(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+    return a;
+}
+
 constexpr int BM = 128;          // query rows per workgroup = one Q scale block
 constexpr int BN = 64;           // keys per tile (half a K/V scale block)
 constexpr int NTHREADS = 256;
@@ -243,6 +250,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
     float m_run = kNegInf;   // running max in scaled base-2 units, same in lane and lane^32
+    float neg_m = 0.f;       // -m_run, or 0 while m_run = -inf
+    float grow_at = kNegInf; // m_run + threshold, or -inf while m_run = -inf
     float l_run = 0.f;
 
     const int kx = kswz(col);
@@ -287,30 +296,34 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         }
     };
     // ---- the row's max over a block in scaled base-2 units (c > 0 keeps the order)
+    //      (three-operand maxima only, which the compiler emits without canonicalising moves;
+    //      c >= FLT_MIN > 0 maps -inf to -inf)
     auto row_max = [&](const f32x16& s, float c) __attribute__((always_inline)) {
-        float a = __builtin_fmaxf(s[0], s[1]);
-        float b = __builtin_fmaxf(s[14], s[15]);
-#pragma unroll
-        for (int j = 2; j < 8; j += 2) a = max3(a, s[j], s[j + 1]);
-#pragma unroll
-        for (int j = 8; j < 14; j += 2) b = max3(b, s[j], s[j + 1]);
-        const float lm = __builtin_fmaxf(a, b);
-        const float mt = fmaxf(lm, swap_halves(lm));
-        return mt == kNegInf ? kNegInf : mt * c;
+        float a = max3(s[0], s[1], s[2]);
+        float b = max3(s[8], s[9], s[10]);
+        a = max3(a, s[3], s[4]);
+        b = max3(b, s[11], s[12]);
+        a = max3(a, s[5], s[6]);
+        b = max3(b, s[13], s[14]);
+        a = max3(a, s[7], s[15]);
+        return max_halves(__builtin_fmaxf(a, b)) * c;
     };
     // ---- online softmax update (lazy: the reference max moves only when it grows by more
-    //      than 2^8 in probability); returns the exponent bias -m + log2 scale_v
+    //      than 2^8 in probability); returns the exponent bias -m + log2 scale_v.  A row grows
+    //      when its block max exceeds grow_at = m_run + threshold, which is -inf while m_run is:
+    //      a first finite max always grows, a row without a visible key yet does not.
     auto softmax_update = [&](float mt, float log2_sv) __attribute__((always_inline)) {
-        const float m_new = fmaxf(m_run, mt);
-        const bool grow = m_new > m_run && (m_run == kNegInf || m_new - m_run > kRescaleThreshold);
-        if (__any(grow)) {
+        if (__any(mt > grow_at)) {
+            const float m_new = fmaxf(m_run, mt);
             const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
             m_run = m_new;
+            neg_m = m_new == kNegInf ? 0.f : -m_new;
+            grow_at = m_new == kNegInf ? kNegInf : m_new + kRescaleThreshold;
         }
-        return (m_run == kNegInf ? 0.f : -m_run) + log2_sv;
+        return neg_m + log2_sv;
     };
     // ---- P'^T = exp2(S^T c + bias) rounded to bf16, as the B operands of two 16-key steps
     auto exp_block = [&](const f32x16& s, float c, float bias, bf16x8 (&pf)[2]) __attribute__((always_inline)) {

@@ -261,16 +261,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
 
     // ---- S^T = K8 Q8^T for the 32-key block kb of a K tile
     //      (MXFP8: `ke` is the exponent word of this lane's key in block kb)
+    //      The lane's two 16-byte chunks per k-step, in Q's channel order (see the Q fragment),
+    //      as byte offsets inside a block: the slot and the block then only add an immediate.
+    uint32_t koff[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int c0 = (MX ? ks * 4 + half : ks * 4 + half * 2) ^ kx;
+        const int c1 = (MX ? ks * 4 + half + 2 : ks * 4 + half * 2 + 1) ^ kx;
+        koff[ks][0] = col * KROWB + c0 * 16;
+        koff[ks][1] = col * KROWB + c1 * 16;
+    }
+    // V fragment offsets of the lane per 32-channel block (the key's swizzle depends only on
+    // the lane's key inside its group of 8, so the step and block only add an immediate)
+    uint32_t voff[CBLK];
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+        const int ch = cb * 32 + vch_l;
+        voff[cb] = vkey_l * VROWB + (((ch >> 3) ^ vswz(vkey_l)) * 16) + (ch & 7) * 2;
+    }
     auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s, uint32_t ke) __attribute__((always_inline)) {
-        const uint8_t* row = kl + (kb * 32 + col) * KROWB;
+        const uint8_t* blk = kl + kb * 32 * KROWB;
         s = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            // 16-byte chunks of the row in Q's channel order (see the Q fragment)
-            const int c0 = (MX ? ks * 4 + half : ks * 4 + half * 2) ^ kx;
-            const int c1 = (MX ? ks * 4 + half + 2 : ks * 4 + half * 2 + 1) ^ kx;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + c0 * 16);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + c1 * 16);
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(blk + koff[ks][0]);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(blk + koff[ks][1]);
             const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
             if constexpr (MX) {
@@ -359,10 +374,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
                 u32x2 part[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int key = kb * 32 + ks * 16 + r * 8 + vkey_l;
-                    const int ch = cb * 32 + vch_l;
-                    const int chunk = (ch >> 3) ^ vswz(key);
-                    part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
+                    const int key0 = kb * 32 + ks * 16 + r * 8;   // multiple of 8: same swizzle
+                    part[r] = lds_read_tr16_b64(vl + key0 * VROWB + voff[cb]);
                 }
                 const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
                 oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);

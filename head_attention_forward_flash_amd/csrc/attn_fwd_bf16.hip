@@ -360,8 +360,8 @@ next_item:
             }
         };
         // ---- this lane's max over its 16 scores of a block
-        //      (three-operand maxima only: a two-operand maximum of scores that may come from the
-        //      mask's select costs two extra canonicalising instructions)
+        //      (three-operand maxima: the compiler puts canonicalising moves before a maximum of
+        //      scores that may come from the mask's select, and fewer of them before v_max3)
         auto lane_max = [&](const f32x16& s) __attribute__((always_inline)) {
             float a = max3(s[0], s[1], s[2]);
             float b = max3(s[8], s[9], s[10]);
@@ -373,7 +373,7 @@ next_item:
             return __builtin_fmaxf(a, b);
         };
         // ---- online softmax update from a block max (the reference max only moves when a row's
-        //      max grows by more than 2^8 in probability); returns m * c for the exponentials
+        //      max grows by more than 2^8 in probability); returns m * c for the exponentials.
         //      A row grows when m_new * c exceeds grow_at = m_run * c + threshold; while m_run is
         //      -inf, grow_at is -inf, so a first finite max always grows and a row that has seen
         //      no key yet (m_new = -inf) does not.  mc_run and grow_at change only on growth, so

@@ -311,8 +311,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         }
     };
     // ---- the row's max over a block in scaled base-2 units (c > 0 keeps the order)
-    //      (three-operand maxima only, which the compiler emits without canonicalising moves;
-    //      c >= FLT_MIN > 0 maps -inf to -inf)
+    //      (three-operand maxima, which need fewer of the compiler's canonicalising moves than
+    //      two-operand ones; c >= FLT_MIN > 0 maps -inf to -inf)
     auto row_max = [&](const f32x16& s, float c) __attribute__((always_inline)) {
         float a = max3(s[0], s[1], s[2]);
         float b = max3(s[8], s[9], s[10]);

@@ -199,3 +199,31 @@ def test_negative_and_zero_scale(dims):
     o, lse = _run(q, k, v, True, 0.0)
     counts = np.arange(1, 151, dtype=np.float64)
     np.testing.assert_allclose(lse[0, 0].numpy(), np.log(counts), atol=2 ** -8)
+
+
+def _ramp_inputs(dqk, dv, s, step, seed, rising):
+    # every query points along channel 0 and key j carries step * j there (reversed when not
+    # rising), so each row's scores climb (or fall) steadily along the keys; the other channels
+    # hold small noise
+    q = workloads.make_random((1, s, 2, dqk), seed, dtype=torch.float32, std=0.05)
+    k = workloads.make_random((1, s, 2, dqk), seed + 1, dtype=torch.float32, std=0.05)
+    q[..., 0] = 1.0
+    j = torch.arange(s, dtype=torch.float32)
+    k[0, :, :, 0] = (step * (j if rising else s - 1 - j))[:, None]
+    v = workloads.make_random((1, s, 2, dv), seed + 2)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+def test_running_max_rising_in_steps(dims):
+    # With a key step of 2^-4, the row max moves by 32 * 2^-4 * scale * log2(e) per 32-key block:
+    # about 2 (scale 0.7, below the 2^8 rescale threshold, so the reference max lags and P
+    # reaches up to 2^8 before a rescale) or about 29 (scale 10, a rescale every block).  Falling
+    # scores fix the max on the first block instead.
+    dqk, dv = dims
+    for rising in (True, False):
+        q, k, v = _ramp_inputs(dqk, dv, 300, 2.0 ** -4, 5000 + dqk, rising)
+        for scale in (0.7, 10.0):
+            for causal in (False, True):
+                _check_all(q, k, v, causal, f"d{dqk} ramp rising={rising} scale={scale} causal={causal}",
+                           scale=scale)

@@ -171,3 +171,19 @@ def test_fp8_deterministic():
     a = _fp8_call(q, k, v, mu, True)
     b = _fp8_call(q, k, v, mu, True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("q0", [4.0, 64.0])
+def test_running_max_rising_in_steps(q0):
+    # Queries point along channel 0 (q0) and key j carries j / 8 there, so each row's scores
+    # climb along the keys by q0 * 4 / sqrt(128) * log2(e) per 32-key block: about 2 for q0 = 4
+    # (below the rescale threshold) and about 33 for q0 = 64 (a rescale every block).
+    d, sq, sk = 128, 256, 384
+    q = workloads.make_random((1, sq, 2, d), 7100, dtype=torch.float32, std=0.05)
+    k = workloads.make_random((1, sk, 2, d), 7101, dtype=torch.float32, std=0.05)
+    q[..., 0] = q0
+    k[0, :, :, 0] = (torch.arange(sk, dtype=torch.float32) / 8.0)[:, None]
+    v = workloads.make_random((1, sk, 2, d), 7102)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    for causal in (False, True):
+        _check_attention(q, k, v, _oracle_mu(k), causal, f"ramp q0={q0} causal={causal}")

@@ -45,7 +45,8 @@
 namespace mha {
 namespace {
 
-// max(x of this lane, x of lane ^ 32): the exchange of max_with_partner followed by one v_max.
+// max(x of this lane, x of lane ^ 32): the exchange of max_with_partner followed by one v_max
+// (x likewise must not come straight from an MFMA).
 __device__ __forceinline__ float max_halves(float x) {
     float a = x, b = x;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));

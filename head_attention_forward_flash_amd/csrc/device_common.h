@@ -94,7 +94,8 @@ __device__ __forceinline__ float swap_halves(float x) {
 // half's x in one register and the upper half's in the other on every lane, so one v_max3 takes
 // the maximum without a lane select.  Written as one asm block: the builtin's second result is
 // miscompiled by this compiler when it is not consumed through a lane select.  The s_nop 1 gives
-// the two wait states a VALU write needs before v_permlane32_swap reads it.
+// the two wait states a VALU write needs before v_permlane32_swap reads it.  The compiler adds no
+// wait states before inline asm for other producers: x and y must not come straight from an MFMA.
 __device__ __forceinline__ float max_with_partner(float x, float y) {
     float a = x, b = x;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max3_f32 %0, %0, %1, %2"

@@ -280,13 +280,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         const int ch = cb * 32 + vch_l;
         voff[cb] = vkey_l * VROWB + (((ch >> 3) ^ vswz(vkey_l)) * 16) + (ch & 7) * 2;
     }
-    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s, uint32_t ke) __attribute__((always_inline)) {
+    // The two K reads of a block's first k-step are issued ahead, at the end of the region B
+    // before the region A that multiplies them (as in the bf16 kernel).
+    using KPre = u32x4[2];
+    auto k_prefetch = [&](const uint8_t* kl, int kb, KPre& pre) __attribute__((always_inline)) {
+        const uint8_t* blk = kl + kb * 32 * KROWB;
+        pre[0] = *reinterpret_cast<const u32x4*>(blk + koff[0][0]);
+        pre[1] = *reinterpret_cast<const u32x4*>(blk + koff[0][1]);
+    };
+    auto qk_block = [&](const uint8_t* kl, int kb, f32x16& s, uint32_t ke, const KPre& pre) __attribute__((always_inline)) {
         const uint8_t* blk = kl + kb * 32 * KROWB;
         s = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(blk + koff[ks][0]);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(blk + koff[ks][1]);
+            const u32x4 a0 = ks == 0 ? pre[0] : *reinterpret_cast<const u32x4*>(blk + koff[ks][0]);
+            const u32x4 a1 = ks == 0 ? pre[1] : *reinterpret_cast<const u32x4*>(blk + koff[ks][1]);
             const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
             if constexpr (MX) {
@@ -394,23 +402,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     // region A: S of the next block (D/64 fp8 MFMAs, two K reads each) under the exponentials of the
     //           current block
     auto region_a = [&](const uint8_t* kl, int kb, uint32_t ke, f32x16& sn, const f32x16& s, float c, float bias,
-                        bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+                        bf16x8 (&pf)[2], const KPre& pre) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        qk_block(kl, kb, sn, ke);
+        qk_block(kl, kb, sn, ke, pre);
         exp_block(s, c, bias, pf);
         // keep the exponentials here: without a use inside the region the compiler would sink
         // them to the P.V MFMAs that consume them
         asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-        sched_region<KS, 2 * KS, 2, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KS>{});
+        // the later k-steps' reads open the region, under the first MFMA
+        sched_region<KS, 2 * (KS - 1), 2 * (KS - 1), 1, EXP_VALU, 0>(std::make_integer_sequence<int, KS>{});
         __builtin_amdgcn_sched_barrier(0);
     };
-    // region B: P.V of the current block under its row sum and the next block's row max
+    // region B: P.V of the current block under its row sum and the next block's row max; with PRE,
+    // it also reads the first k-step of the next region A's K block
     auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], float inv_sv, const f32x16& sn,
-                        float c_next, auto vmem_c) __attribute__((always_inline)) {
+                        float c_next, auto vmem_c, auto pre_c, const uint8_t* kl_next, int kb_next,
+                        KPre& pre) __attribute__((always_inline)) {
+        constexpr int NPRE = decltype(pre_c)::value ? 2 : 0;
         pv_block(vl, kb, pf);
         row_sum(pf, inv_sv);
         const float mt = row_max(sn, c_next);
-        sched_region<PV_MFMA, 2 * PV_MFMA, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+        if constexpr (NPRE > 0) k_prefetch(kl_next, kb_next, pre);
+        sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
             std::make_integer_sequence<int, PV_MFMA>{});
         __builtin_amdgcn_sched_barrier(0);
         return mt;
@@ -424,7 +437,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     using DmaVmem = std::integral_constant<int, KDMA + VDMA + (MX ? 2 : 0)>;
     // (MXFP8: ke[0] holds the exponent words of tile t, ke[1] those of tile t+1; the words of
     // tile t+2 are loaded with its K tile)
-    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc, u32x2 (&ke)[2])
+    using Pre = std::true_type;
+    using NoPre = std::false_type;
+    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc, u32x2 (&ke)[2], KPre& pre)
                          __attribute__((always_inline)) {
         using Cur = std::integral_constant<int, decltype(par_c)::value>;
         using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         bf16x8 pf[2];
         // block 2t (exponentials, P.V) with block 2t+1 (S, max)
         float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s, sc.c, bias, pf);
+        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s, sc.c, bias, pf, pre);
         if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
@@ -442,31 +457,32 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         if constexpr (MX) ke_new = kexp_load(t + 2);
         issue_k(t + 2, k_slot(Cur{}));
         issue_v(t + 1, v_slot(Nxt{}));
-        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{});
+        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
         // block 2t+1 (now in sn) with block 2t+2 (the first block of the next tile), whose S goes
         // into s: the two score buffers swap roles instead of being copied
         bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Nxt{}), 0, ke[1][0], s, sn, sc.c, bias, pf);
+        region_a(k_slot(Nxt{}), 0, ke[1][0], s, sn, sc.c, bias, pf, pre);
         if (need_mask(2 * t + 2)) mask_block(2 * t + 2, s);
         __builtin_amdgcn_sched_barrier(0);
-        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, s, sc_next.c, NoVmem{});
+        // the next region A (an iteration or the last tile) starts on block 1 of K_{t+1}
+        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, s, sc_next.c, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
         sc = sc_next;
         ke[0] = ke[1];
         ke[1] = ke_new;
     };
     // the last tile: its two blocks, nothing further to load
-    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc, const u32x2 (&ke)[2])
-                    __attribute__((always_inline)) {
+    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc, const u32x2 (&ke)[2],
+                    KPre& pre) __attribute__((always_inline)) {
         using Cur = std::integral_constant<int, decltype(par_c)::value>;
         f32x16 sn;
         bf16x8 pf[2];
         float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s0, sc.c, bias, pf);
+        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s0, sc.c, bias, pf, pre);
         if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, NoVmem{});
+        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, NoVmem{}, NoPre{}, nullptr, 0, pre);
         bias = softmax_update(mt, sc.log2_sv);
         exp_block(sn, sc.c, bias, pf);
         row_sum(pf, sc.inv_sv);
@@ -488,19 +504,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         __syncthreads();
         TileScale sc = tile_scale(0);
         f32x16 s;
-        qk_block(k_slot(Zero{}), 0, s, ke[0][0]);
+        KPre pre;
+        k_prefetch(k_slot(Zero{}), 0, pre);
+        qk_block(k_slot(Zero{}), 0, s, ke[0][0], pre);
         if (need_mask(0)) mask_block(0, s);
         float mt = row_max(s, sc.c);
+        k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_0
         int t = 0;
         for (; t + 2 < ntiles; t += 2) {
-            iteration(t, Zero{}, s, mt, sc, ke);
-            iteration(t + 1, One{}, s, mt, sc, ke);
+            iteration(t, Zero{}, s, mt, sc, ke, pre);
+            iteration(t + 1, One{}, s, mt, sc, ke, pre);
         }
         if (t + 1 < ntiles) {
-            iteration(t, Zero{}, s, mt, sc, ke);
-            last(t + 1, One{}, s, mt, sc, ke);
+            iteration(t, Zero{}, s, mt, sc, ke, pre);
+            last(t + 1, One{}, s, mt, sc, ke, pre);
         } else {
-            last(t, Zero{}, s, mt, sc, ke);
+            last(t, Zero{}, s, mt, sc, ke, pre);
         }
     }
 

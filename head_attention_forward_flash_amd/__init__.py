@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "mha_fwd_bf16", "mha_fwd_bf16_varlen", "mha_fwd_bf16_window_sink", "mha_fwd_bf16_varlen_window_sink",
     "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
-    "mha_fwd_mxfp8", "mha_status_string", "mha_last_error",
+    "mha_fwd_mxfp8", "mha_status_string", "mha_last_error", "mha_debug_sync_enabled",
 )
 
 
@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_status_string.argtypes = [i32]
     lib.mha_last_error.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []
+    lib.mha_debug_sync_enabled.restype = i32
+    lib.mha_debug_sync_enabled.argtypes = []
     _lib = lib
     return lib
 
@@ -129,10 +131,58 @@ def _stream(device) -> int:
 
 
 def _require_device(*tensors):
-    torch = _torch()
     for t in tensors:
         if t is not None and t.device.type != "cuda":
             raise ValueError("tensors must live on a ROCm device (torch 'cuda' device)")
+
+
+def _dims(name, t, ndim):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected a {ndim}-d tensor, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _expect(name, t, shape, dtype, device):
+    """Refuse a tensor whose shape, dtype or device does not match what the call was sized from:
+    the library trusts the sizes it is given, so a short buffer would be read or written past
+    its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+
+
+def _expect_workspace(name, ws, need, device):
+    torch = _torch()
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-d uint8 tensor")
+    if ws.device != device:
+        raise ValueError(f"{name} is on {ws.device}, the other tensors on {device}")
+    if ws.numel() < need:
+        raise ValueError(f"{name} holds {ws.numel()} bytes, the call needs {need}")
+
+
+def _attn_shapes(q, k, v, out, ndim):
+    """Sizes of an attention call, every tensor checked against them (BSHD: ndim 4, THD: 3)."""
+    torch = _torch()
+    qs, ks, vs = _dims("q", q, ndim), _dims("k", k, ndim), _dims("v", v, ndim)
+    d_qk, d_v = qs[-1], vs[-1]
+    lead_q, lead_k = qs[:-2], ks[:-2]       # (b, sq) or (total_q,); (b, sk) or (total_k,)
+    hq, hk = qs[-2], ks[-2]
+    if ndim == 4 and ks[0] != qs[0]:
+        raise ValueError(f"k: batch {ks[0]} differs from q's {qs[0]}")
+    _expect("q", q, qs, torch.bfloat16, q.device)
+    _expect("k", k, lead_k + (hk, d_qk), torch.bfloat16, q.device)
+    _expect("v", v, lead_k + (hk, d_v), torch.bfloat16, q.device)
+    if out is not None:
+        _expect("out", out, lead_q + (hq, d_v), torch.bfloat16, q.device)
+    return qs, ks, d_v
 
 
 def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
@@ -140,13 +190,8 @@ def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] =
     """Fused attention forward in bf16. Returns (o, lse) with lse [b, hq, sq] fp32 (or None)."""
     torch = _torch()
     lib = load_library()
-    _require_device(q, k, v, out)
-    b, sq, hq, d_qk = q.shape
-    _, sk, hk, _ = k.shape
-    d_v = v.shape[3]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
+    (b, sq, hq, d_qk), (_, sk, hk, _), d_v = _attn_shapes(q, k, v, out, 4)
+    _require_device(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     if out is None:
@@ -164,15 +209,12 @@ def mha_fwd_bf16_window_sink(q, k, v, causal: bool = False, window_left: int = -
     (fp32 [hq] on the device, or None). Returns (o, lse)."""
     torch = _torch()
     lib = load_library()
-    _require_device(q, k, v, out, sinks)
-    b, sq, hq, d_qk = q.shape
-    _, sk, hk, _ = k.shape
-    d_v = v.shape[3]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
-    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous()):
-        raise ValueError("sinks must be a contiguous float32 tensor of hq elements")
+    (b, sq, hq, d_qk), (_, sk, hk, _), d_v = _attn_shapes(q, k, v, out, 4)
+    if sinks is not None:
+        _expect("sinks", sinks, (hq,), torch.float32, q.device)
+        if not sinks.is_contiguous():
+            raise ValueError("sinks must be contiguous")
+    _require_device(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     if out is None:
@@ -202,21 +244,19 @@ def mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     mha_fwd_bf16_varlen_window_sink."""
     torch = _torch()
     lib = load_library()
-    _require_device(q, k, v, out, cu_seqlens_q, cu_seqlens_k, sinks)
-    total_q, hq, d_qk = q.shape
-    total_k, hk, _ = k.shape
-    d_v = v.shape[2]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
+    (total_q, hq, d_qk), (total_k, hk, _), d_v = _attn_shapes(q, k, v, out, 3)
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 1-d int32 tensor")
-    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous()):
-        raise ValueError("sinks must be a contiguous float32 tensor of hq elements")
+        _expect(name, t, (_dims(name, t, 1)[0],), torch.int32, q.device)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if sinks is not None:
+        _expect("sinks", sinks, (hq,), torch.float32, q.device)
+        if not sinks.is_contiguous():
+            raise ValueError("sinks must be contiguous")
     b = cu_seqlens_q.numel() - 1
     if b < 0 or cu_seqlens_k.numel() != b + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold b + 1 offsets")
+    _require_device(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     if out is None:
@@ -241,13 +281,15 @@ def k_smooth_mean(k, key_stride: int = 1, max_keys: int = 0, tau: float = 0.25, 
     """K-smoothing gate. Returns (mean [b, hk, d] fp32, gate [b, hk] int32)."""
     torch = _torch()
     lib = load_library()
+    ks = _dims("k", k, 4)
+    _expect("k", k, ks, torch.bfloat16, k.device)
+    b, sk, hk, d = ks
+    need = k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys)
+    if workspace is not None:
+        _expect_workspace("workspace", workspace, need, k.device)
     _require_device(k)
-    if k.dtype != torch.bfloat16:
-        raise ValueError("k must be bfloat16")
-    b, sk, hk, d = k.shape
     mean = torch.empty((b, hk, d), dtype=torch.float32, device=k.device)
     gate = torch.empty((b, hk), dtype=torch.int32, device=k.device)
-    need = k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
     _check(lib.k_smooth_mean(_ptr(k), _bshd_strides(k), b, hk, sk, d, key_stride, max_keys, float(tau),
@@ -269,19 +311,24 @@ def mha_fp8_workspace_layout(b, hq, hk, sq, sk, d):
 
 def _fwd_quantised(entry, need_fn, q, k, v, k_mean, causal, softmax_scale, out, lse, workspace):
     torch = _torch()
-    _require_device(q, k, v, k_mean, out)
-    b, sq, hq, d = q.shape
-    _, sk, hk, _ = k.shape
+    (b, sq, hq, d), (_, sk, hk, _), d_v = _attn_shapes(q, k, v, out, 4)
+    if d_v != d:
+        raise ValueError(f"v: head dim {d_v} differs from q/k's {d} (the quantised call has one head dim)")
+    if k_mean is not None:
+        _expect("k_mean", k_mean, (b, hk, d), torch.float32, q.device)
+        if not k_mean.is_contiguous():
+            raise ValueError("k_mean must be contiguous")
+    need = need_fn(b, hq, hk, sq, sk, d)
+    if workspace is not None:
+        _expect_workspace("workspace", workspace, need, q.device)
+    _require_device(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((b, sq, hq, d), dtype=torch.bfloat16, device=q.device)
     lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
-    need = need_fn(b, hq, hk, sq, sk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if k_mean is not None and (k_mean.dtype != torch.float32 or not k_mean.is_contiguous()):
-        raise ValueError("k_mean must be a contiguous float32 [b, hk, d] tensor")
     _check(entry(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
                  _ptr(k_mean), _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d,
                  float(softmax_scale), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream(q.device)))

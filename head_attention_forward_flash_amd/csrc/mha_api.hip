@@ -9,6 +9,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/mha.h"
@@ -33,10 +35,29 @@ mha_status ok() {
     return MHA_OK;
 }
 
-mha_status hip_status(hipError_t e, const char* what) {
-    if (e == hipSuccess) return ok();
-    return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+// MHA_DEBUG_SYNC, read once per process: set to anything but "" or "0", every launch is
+// followed by a synchronisation of its stream, so that a kernel fault is reported by the call
+// that launched the kernel instead of surfacing in a later, unrelated one.
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = std::getenv("MHA_DEBUG_SYNC");
+        return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+    }();
+    return on;
 }
+
+// Status of a launch just enqueued on `stream` (with MHA_DEBUG_SYNC, of its execution too).
+mha_status launched(hipError_t e, const char* what, void* stream) {
+    if (e != hipSuccess) return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (debug_sync()) {
+        e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(MHA_ERR_HIP, "%s: failed in execution (MHA_DEBUG_SYNC): %s", what, hipGetErrorString(e));
+    }
+    return ok();
+}
+
 
 constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;
 
@@ -110,6 +131,8 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
+int mha_debug_sync_enabled(void) { return debug_sync() ? 1 : 0; }
+
 }  // extern "C"
 
 namespace {
@@ -169,8 +192,8 @@ mha_status fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_stri
     p.window_left = window_left >= sq ? -1 : window_left;
     p.window_right = (causal || window_right >= sk) ? -1 : window_right;
     p.sinks = sinks;
-    return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
-                      "attn_fwd_bf16 launch");
+    return launched(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
+                    "attn_fwd_bf16", stream);
 }
 
 }  // namespace
@@ -263,8 +286,8 @@ mha_status fwd_bf16_varlen(const void* q, mha_strides q_stride, const void* k, m
     p.window_left = window_left >= max_seqlen_q ? -1 : window_left;
     p.window_right = (causal || window_right >= max_seqlen_k) ? -1 : window_right;
     p.sinks = sinks;
-    return hip_status(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
-                      "attn_fwd_bf16 (varlen) launch");
+    return launched(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
+                    "attn_fwd_bf16 (varlen)", stream);
 }
 
 }  // namespace
@@ -342,7 +365,7 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int
     p.mean = mean;
     p.gate = gate;
     p.aligned = (kaddr % 16 == 0) && (k_stride.b % 8 == 0) && (k_stride.s % 8 == 0) && (k_stride.h % 8 == 0);
-    return hip_status(mha::launch_k_smooth_mean(p, static_cast<hipStream_t>(stream)), "k_smooth_mean launch");
+    return launched(mha::launch_k_smooth_mean(p, static_cast<hipStream_t>(stream)), "k_moments / k_fold_gate", stream);
 }
 
 mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets) {
@@ -473,8 +496,8 @@ mha_status fwd_quantised(bool mx, const void* q, mha_strides q_stride, const voi
         qvv = quant(v, vv, nullptr, hk, sk, nk, off[2], int64_t(off[5]), true);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = mha::launch_quant_fp8(qq, qk, qvv, s);
-    if (e != hipSuccess) return hip_status(e, "quant_fp8 launch");
+    st = launched(mha::launch_quant_fp8(qq, qk, qvv, s), "quant_fp8", stream);
+    if (st != MHA_OK) return st;
 
     mha::Fp8AttnParams p{};
     p.q = qq.codes;
@@ -500,7 +523,7 @@ mha_status fwd_quantised(bool mx, const void* q, mha_strides q_stride, const voi
     p.nk = static_cast<int>(nk);
     p.n_mblocks = static_cast<int>(nq);
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
-    return hip_status(mha::launch_attn_fwd_fp8(p, d, causal != 0, s), "attn_fwd_fp8 launch");
+    return launched(mha::launch_attn_fwd_fp8(p, d, causal != 0, s), "attn_fwd_fp8", stream);
 }
 
 }  // namespace

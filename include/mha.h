@@ -308,6 +308,20 @@ const char* mha_status_string(mha_status status);
 /* Thread-local message of the last refusal or failure on this thread ("" if none). */
 const char* mha_last_error(void);
 
+/*
+ * mha_debug_sync_enabled - whether the debug synchronisation switch is on (1) or off (0).
+ *
+ * The switch is the environment variable MHA_DEBUG_SYNC, read once, at the first call into the
+ * library that needs it: any value other than "" or "0" turns it on.  Then every entry point
+ * synchronises its stream after each kernel it launches and returns MHA_ERR_HIP, naming the
+ * kernel, if that kernel failed while running.  Without it a kernel fault only surfaces at a
+ * later synchronisation, often inside an unrelated launch: the failure mode described in
+ * "MHA v4: fixes, refactor, new kernel, perf tweaks" (review comments, faults that surface
+ * asynchronously in a later launch).  Costs one stream synchronisation per kernel; for
+ * debugging only.
+ */
+int mha_debug_sync_enabled(void);
+
 #ifdef __cplusplus
 }
 #endif

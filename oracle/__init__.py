@@ -40,7 +40,7 @@ outside this package: closed forms, hand-derived examples under
 torch's float8_e4m3fn cast, numpy's mean/var) and brute force.
 """
 
-from .attention import attention_forward, attention_flops, attention_varlen  # noqa: F401
+from .attention import attention_forward, attention_varlen  # noqa: F401
 from .gate import k_smooth_mean, key_sample  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,

@@ -25,12 +25,6 @@ from __future__ import annotations
 import numpy as np
 
 
-def attention_flops(b, hq, sq, sk, d_qk, d_v, causal):
-    """Algorithmic FLOPs of one forward: 2*b*hq*sq*sk*(d_qk+d_v), halved when causal."""
-    f = 2.0 * b * hq * sq * sk * (d_qk + d_v)
-    return f / 2.0 if causal else f
-
-
 def attention_forward(q, k, v, *, scale, causal, heads=None, rows=None, batches=None):
     """Plain attention forward in float64.
 

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import workloads
-from parity import (assert_bf16_parity, oracle_heads, require_gpu, scale_for, to_np)
+from parity import (assert_bf16_parity, assert_every_block_row, oracle_heads, require_gpu, scale_for, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,8 @@ def test_multi_tile_ragged(shape, causal):
 
 
 def _full_size_sampled(name, heads, nrows, seed):
+    """The full-size launch: many seeded rows (and the block edges) of a few heads, plus one
+    seeded row of every (batch, head, 128-row block), i.e. of every workgroup."""
     w = workloads.WORKLOADS[name]
     q, k, v = workloads.make_qkv(w)
     o, lse = _run(q, k, v, w.causal, w.scale)
@@ -67,6 +69,7 @@ def _full_size_sampled(name, heads, nrows, seed):
         o_g = to_np(o[bb][rows][:, heads])
         l_g = lse[bb][heads][:, rows].numpy().astype(np.float64)
         assert_bf16_parity(o_g, o_ref, l_g, l_ref, f"{name} b={bb} heads={heads}")
+    assert_every_block_row(q, k, v, o, lse, scale=w.scale, causal=w.causal, seed=seed, what=name)
 
 
 def test_full_gqa_d64_causal_sampled():
@@ -93,6 +96,17 @@ def test_full_gqa_d128_8192_causal_sampled():
 
 def test_full_mla_tp8_causal_sampled():
     _full_size_sampled("mla_d192_d128_tp8_causal", [0, 15], 160, 12)
+
+
+def test_full_gqa8_d128_tp8_noncausal_sampled():
+    # one rank's share of 8-way head sharding of a 64-query-head, 8-kv-head model: 8 query heads
+    # on one kv head (GQA 8:1)
+    _full_size_sampled("gqa8_d128_tp8_noncausal", [0, 3, 7], 128, 13)
+
+
+def test_full_gqa5_d128_tp8_noncausal_sampled():
+    # 40 query heads over 8 kv heads, one rank of 8: 5 query heads on one kv head (GQA 5:1)
+    _full_size_sampled("gqa5_d128_tp8_noncausal", [0, 2, 4], 128, 14)
 
 
 def test_value_ones_gives_ones():

@@ -94,6 +94,16 @@ WORKLOADS = {
     "mla_d192_d128_tp8_causal": Workload(
         "mla_d192_d128_tp8_causal", b=1, hq=16, hk=16, sq=8192, sk=8192, d_qk=192, d_v=128, causal=True,
         seed=108, description="b1 hq16 hk16 8192^2 dqk192 dv128 causal bf16 (one rank of 8-way head sharding)"),
+    # The retune page's two real-model d128 regressions ("The 8 remaining regressions" table):
+    # 8192^2 d128 non-causal ("dense(c0)") with per-rank HQ/HK of 8/1 and 5/1 at TP8, i.e. one
+    # GPU's share of 8-way head sharding of models with 64/8 and 40/8 query/kv heads (batch not
+    # printed, b = 1 here)
+    "gqa8_d128_tp8_noncausal": Workload(
+        "gqa8_d128_tp8_noncausal", b=1, hq=8, hk=1, sq=8192, sk=8192, d_qk=128, d_v=128, causal=False,
+        seed=115, description="b1 hq8 hk1 8192^2 d128 non-causal bf16 (one rank of 8-way head sharding)"),
+    "gqa5_d128_tp8_noncausal": Workload(
+        "gqa5_d128_tp8_noncausal", b=1, hq=5, hk=1, sq=8192, sk=8192, d_qk=128, d_v=128, causal=False,
+        seed=116, description="b1 hq5 hk1 8192^2 d128 non-causal bf16 (one rank of 8-way head sharding)"),
     "fp8_long_h5": Workload(
         "fp8_long_h5", b=1, hq=5, hk=5, sq=65536, sk=65536, d_qk=128, d_v=128, causal=False,
         seed=109, fp8=True, k_bias_std=3.0,

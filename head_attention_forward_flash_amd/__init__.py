@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "mha_fwd_bf16", "mha_fwd_bf16_varlen", "mha_fwd_bf16_window_sink", "mha_fwd_bf16_varlen_window_sink",
     "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
-    "mha_fwd_mxfp8", "mha_status_string", "mha_last_error", "mha_debug_sync_enabled",
+    "mha_fwd_mxfp8", "mha_status_string", "mha_last_error", "mha_debug_sync_enabled", "k_smooth_mean_noalloc",
 )
 
 
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.k_smooth_mean_workspace_bytes.argtypes = [i32] * 6
     lib.k_smooth_mean.restype = i32
     lib.k_smooth_mean.argtypes = [vp, Strides, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.k_smooth_mean_noalloc.restype = i32
+    lib.k_smooth_mean_noalloc.argtypes = [vp, Strides, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.mha_fwd_fp8_workspace_bytes.restype = sz
     lib.mha_fwd_fp8_workspace_bytes.argtypes = [i32] * 6
     lib.mha_fp8_workspace_layout.restype = i32
@@ -294,6 +296,29 @@ def k_smooth_mean(k, key_stride: int = 1, max_keys: int = 0, tau: float = 0.25, 
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
     _check(lib.k_smooth_mean(_ptr(k), _bshd_strides(k), b, hk, sk, d, key_stride, max_keys, float(tau),
                              _ptr(mean), _ptr(gate), _ptr(workspace), workspace.numel(), _stream(k.device)))
+    return mean, gate
+
+
+def k_smooth_mean_noalloc(k, key_stride: int = 1, max_keys: int = 0, tau: float = 0.25, mean=None, gate=None):
+    """k_smooth_mean on the library's per-GPU scratch (no workspace; nothing allocated when
+    `mean` and `gate` are given). Returns (mean [b, hk, d] fp32, gate [b, hk] int32)."""
+    torch = _torch()
+    lib = load_library()
+    ks = _dims("k", k, 4)
+    _expect("k", k, ks, torch.bfloat16, k.device)
+    b, sk, hk, d = ks
+    for name, t, shape, dt in (("mean", mean, (b, hk, d), torch.float32), ("gate", gate, (b, hk), torch.int32)):
+        if t is not None:
+            _expect(name, t, shape, dt, k.device)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    _require_device(k)
+    if mean is None:
+        mean = torch.empty((b, hk, d), dtype=torch.float32, device=k.device)
+    if gate is None:
+        gate = torch.empty((b, hk), dtype=torch.int32, device=k.device)
+    _check(lib.k_smooth_mean_noalloc(_ptr(k), _bshd_strides(k), b, hk, sk, d, key_stride, max_keys, float(tau),
+                                     _ptr(mean), _ptr(gate), _stream(k.device)))
     return mean, gate
 
 

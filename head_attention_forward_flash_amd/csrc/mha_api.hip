@@ -11,7 +11,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/mha.h"
 #include "kernels.h"
@@ -57,7 +59,6 @@ mha_status launched(hipError_t e, const char* what, void* stream) {
     }
     return ok();
 }
-
 
 constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;
 
@@ -323,9 +324,44 @@ size_t k_smooth_mean_workspace_bytes(int b, int hk, int sk, int d, int key_strid
     return align256(size_t(b) * hk * (chunks > 0 ? chunks : 1) * 2 * d * sizeof(float));
 }
 
-mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int sk, int d, int key_stride,
-                         int max_keys, float tau, float* mean, int32_t* gate, void* ws, size_t ws_bytes,
-                         void* stream) {
+}  // extern "C"
+
+// Scratch of k_smooth_mean_noalloc: the per-chunk moments live here instead of in a caller's
+// workspace, for callers that cannot allocate.  One copy per GPU, held until the process ends;
+// every call on a GPU shares it.
+static constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_lock;
+std::vector<void*> g_scratch_ptr;   // device address of `scratch`, per device id
+
+// The device address of the current device's copy of `scratch`, looked up on the first call on
+// that device (with that device current).  The array's name is a host-side stand-in: only this
+// address may be handed to kernels.
+mha_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MHA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> g(g_scratch_lock);
+    if (dev >= static_cast<int>(g_scratch_ptr.size())) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(MHA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MHA_OK;
+}
+
+// The gate of both entry points: `ws` is the caller's workspace, or with `noalloc` the
+// library's scratch (then ws / ws_bytes are ignored).
+mha_status gate_call(const void* k, mha_strides k_stride, int b, int hk, int sk, int d, int key_stride,
+                     int max_keys, float tau, float* mean, int32_t* gate, void* ws, size_t ws_bytes, bool noalloc,
+                     void* stream) {
     if (b < 0 || sk < 0) return fail(MHA_ERR_SHAPE, "b, sk must be >= 0 (b=%d sk=%d)", b, sk);
     if (hk < 1) return fail(MHA_ERR_SHAPE, "hk must be >= 1 (hk=%d)", hk);
     if (d != 64 && d != 128 && d != 256) return fail(MHA_ERR_UNSUPPORTED, "d = %d not built; supported: 64 128 256", d);
@@ -342,6 +378,14 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int
     mha_status st = make_view("k", k, k_stride, hk, sk, d, 2, false, &p.kv);
     if (st != MHA_OK) return st;
     const size_t need = k_smooth_mean_workspace_bytes(b, hk, sk, d, key_stride, max_keys);
+    if (noalloc) {
+        if (need > kScratchBytes)
+            return fail(MHA_ERR_WORKSPACE,
+                        "the moments need %zu bytes of scratch, above the %zu bytes the library holds per GPU "
+                        "(lower max_keys, or call k_smooth_mean with a workspace)", need, kScratchBytes);
+        if ((st = scratch_address(&ws)) != MHA_OK) return st;
+        ws_bytes = kScratchBytes;
+    }
     if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);
     if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
     if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
@@ -366,6 +410,21 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int
     p.gate = gate;
     p.aligned = (kaddr % 16 == 0) && (k_stride.b % 8 == 0) && (k_stride.s % 8 == 0) && (k_stride.h % 8 == 0);
     return launched(mha::launch_k_smooth_mean(p, static_cast<hipStream_t>(stream)), "k_moments / k_fold_gate", stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status k_smooth_mean(const void* k, mha_strides k_stride, int b, int hk, int sk, int d, int key_stride,
+                         int max_keys, float tau, float* mean, int32_t* gate, void* ws, size_t ws_bytes,
+                         void* stream) {
+    return gate_call(k, k_stride, b, hk, sk, d, key_stride, max_keys, tau, mean, gate, ws, ws_bytes, false, stream);
+}
+
+mha_status k_smooth_mean_noalloc(const void* k, mha_strides k_stride, int b, int hk, int sk, int d, int key_stride,
+                                 int max_keys, float tau, float* mean, int32_t* gate, void* stream) {
+    return gate_call(k, k_stride, b, hk, sk, d, key_stride, max_keys, tau, mean, gate, nullptr, 0, true, stream);
 }
 
 mha_status mha_fp8_workspace_layout(int b, int hq, int hk, int sq, int sk, int d, size_t* offsets) {

@@ -213,6 +213,26 @@ mha_status k_smooth_mean(const void* k, mha_strides k_stride,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * k_smooth_mean_noalloc - k_smooth_mean without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * Same arguments, results and errors as k_smooth_mean, minus ws / ws_bytes: the per-chunk
+ * moments go to a scratch array the library holds in each GPU's memory (4 MiB per GPU, kept
+ * until the process ends).  It allocates nothing.  Calls whose moments need more than 4 MiB,
+ * i.e. k_smooth_mean_workspace_bytes(...) > 4194304 (b * hk * ceil(T / 256) * 2 * d * 4 bytes,
+ * T the sample count), are refused with MHA_ERR_WORKSPACE and launch nothing.
+ * Every call on one GPU shares that GPU's scratch, whatever the stream: calls that overlap
+ * in time on one GPU (concurrent streams, host threads) race and may give wrong results;
+ * calls in one stream order are safe.  The scratch needs no clearing: each call overwrites
+ * every moment it reads.
+ */
+mha_status k_smooth_mean_noalloc(const void* k, mha_strides k_stride,
+                                 int b, int hk, int sk, int d,
+                                 int key_stride, int max_keys, float tau,
+                                 float* mean, int32_t* gate, void* stream);
+
+/*
  * mha_fwd_fp8 - attention forward on E4M3-quantised, K-smoothed inputs: the
  * quantised mha_v4 call with the FP8 hd128 recipe of "[HIP] Mha v4: run the
  * K-smoothing gate as one HIP call" (Performance table) and "MHA v4: fixes,

@@ -21,9 +21,9 @@
 //          for conflict-free reads: K rows feed the A operand of S^T with one
 //          ds_read_b128 per MFMA, V rows feed the A operand of O^T through
 //          transposing reads (ds_read_b64_tr_b16).
-//   loop   software-pipelined across tiles: while the exponentials of tile t
-//          run on the VALU, the MFMAs of S for tile t+1 already run, and the
-//          lane max of S_{t+1} is taken under the P.V MFMAs of tile t.  The
+//   loop   software-pipelined across 32-key blocks: the S MFMAs of block u+1
+//          run under the last exponentials of block u and its row sum, the P.V
+//          MFMAs of block u under the first exponentials of block u+1.  The
 //          instruction interleaving is fixed with scheduling group barriers, and
 //          the DMA of later tiles is spread over the MFMA stream so no wave stalls
 //          on a full address queue.
@@ -32,10 +32,16 @@
 //          setting the score to -inf, which the exponential maps to exactly 0.
 //   softmax online, in base 2: p = exp2(s*c - m*c) with c = |scale| * log2 e
 //          (at least FLT_MIN, so that a zero scale still maps -inf to 0) folded
-//          into one FMA (a negative scale negates Q, which is exact); the running
-//          max only moves when a row's max grows by more than a factor 2^8 in
-//          probability, which keeps O and l consistent and rescales rarely; the
-//          row sum adds the bf16-rounded probabilities that enter P.V
+//          into one FMA (a negative scale negates Q, which is exact).  m is a
+//          reference max, not the running one: a row takes the max of its first
+//          block, and each later block's exponentials run against the reference
+//          as it stands.  The block's sum of probabilities, which the row sum
+//          needs anyway, then checks it: at most 2^8 per lane means no
+//          probability above 2^8 (the reference lags the row max by at most 8 in
+//          log2 units, as a lazy rescale would keep it); above, the block takes
+//          its own max as the new reference, O and l are rescaled and the block's
+//          exponentials rerun.  No per-block max is taken on the common path.
+//          The row sum adds the bf16-rounded probabilities that enter P.V
 //          (v_dot2_f32_bf16), so O is normalised by exactly the weights it was
 //          built from.
 //
@@ -51,7 +57,11 @@
 namespace mha {
 namespace {
 
-constexpr float kRescaleThreshold = 8.0f;      // log2 units
+// A lane's sum of the 16 rounded probabilities of a block it computed against the reference max;
+// at most this, each probability is at most 2^8 (the reference lags the row max by at most 8 in
+// log2 units), otherwise the block takes a new reference.
+constexpr float kSumLimit = 256.0f;
+template <int N> using IC = std::integral_constant<int, N>;
 constexpr float kMinScale = 1.17549435e-38f;   // FLT_MIN
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
@@ -75,7 +85,7 @@ template <int MFMAS, int DS_TOTAL, int DS_PRE, int DS_PER, int VALU, int VMEM, i
 __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     constexpr int DS_SLOTS = (DS_TOTAL - DS_PRE) / DS_PER;
     constexpr int VALU_PER = (VALU + MFMAS - 1) / MFMAS;
-    constexpr int VALU_SLOTS = (VALU + VALU_PER - 1) / VALU_PER;
+    constexpr int VALU_SLOTS = VALU_PER > 0 ? (VALU + VALU_PER - 1) / VALU_PER : 0;
     if constexpr (DS_PRE > 0) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PRE, 0);
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
@@ -83,11 +93,19 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 // Tile shape per head-dim pair: BM query rows per workgroup (32 per wave), BN keys per tile.
 // 128-row workgroups run two (d128) to four (d32) per CU; the 256-row one runs alone with 8
 // waves, which halves the K/V traffic per FLOP of the wide d192/d128 tiles.
+// EARLY: score pairs (of the 8 per lane and block) of block u+1 whose exponentials run under the
+// P.V MFMAs of block u; the other pairs, the block sum and its check run under the S MFMAs of
+// block u+2.  The wide heads split the VALU work between the two regions about as their MFMAs
+// split; the narrow ones, whose P.V and S regions are short, put all of it under P.V, which also
+// keeps d64 within 168 VGPRs (three workgroups per CU).
+#ifndef MHA_EARLY_WIDE
+#define MHA_EARLY_WIDE 4
+#endif
 template <int DQK, int DV> struct TileCfg;
-template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64; };
-template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64; };
-template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64; };
-template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64; };
+template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64, EARLY = 8; };
+template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, EARLY = 8; };
+template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, EARLY = MHA_EARLY_WIDE; };
+template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, EARLY = MHA_EARLY_WIDE; };
 
 // EXT: sliding window (keys j with i - window_left <= j <= i + window_right, positions inside
 // the sequence) and per-head sink logits.
@@ -292,10 +310,11 @@ next_item:
         f32x16 oacc[CBLK];
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
-        float m_run = kNegInf;   // running max of raw scores, same in lane and lane^32
+        float m_run = kNegInf;   // reference max of raw scores, same in lane and lane^32
         float l_run = 0.f;       // this lane's partial row sum over its half of the keys
         float mc_run = 0.f;      // m_run * c, or 0 while m_run = -inf
-        float grow_at = kNegInf; // mc_run + threshold, or -inf while m_run = -inf
+        float lim = -1.f;        // largest block sum that keeps the reference: kSumLimit, or -1
+                                 // while m_run = -inf (then every block takes a reference)
 
         // fragment addresses inside a slot (bytes)
         const int kx = kswz(col);                     // the row's chunk swizzle (same for every block)
@@ -372,56 +391,75 @@ next_item:
             a = max3(a, s[7], s[15]);
             return __builtin_fmaxf(a, b);
         };
-        // ---- online softmax update from a block max (the reference max only moves when a row's
-        //      max grows by more than 2^8 in probability); returns m * c for the exponentials.
-        //      A row grows when m_new * c exceeds grow_at = m_run * c + threshold; while m_run is
-        //      -inf, grow_at is -inf, so a first finite max always grows and a row that has seen
-        //      no key yet (m_new = -inf) does not.  mc_run and grow_at change only on growth, so
-        //      the common path is one exchange, one three-operand max, a multiply, a compare and
-        //      a branch.
-        auto softmax_update = [&](float mx) __attribute__((always_inline)) {
-            const float m_new = max_with_partner(mx, m_run);
-            const bool grow = m_new * c > grow_at;
-            if (__any(grow)) {
-                const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
-                l_run *= alpha;
+        // ---- the reference max: set from a block's scores (with the partner lane's half of the
+        //      row), moving O and l to the new reference.  Only the first block of a row and the
+        //      rare blocks that fail the check below come here.
+        auto rebase = [&](const f32x16& s) __attribute__((always_inline)) {
+            const float m_new = max_with_partner(lane_max(s), m_run);
+            const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
 #pragma unroll
-                for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-                m_run = m_new;
-                mc_run = m_new == kNegInf ? 0.f : m_new * c;
-                grow_at = m_new == kNegInf ? kNegInf : mc_run + kRescaleThreshold;
-            }
-            return mc_run;
+            for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+            m_run = m_new;
+            mc_run = m_new == kNegInf ? 0.f : m_new * c;
+            lim = m_new == kNegInf ? -1.f : kSumLimit;
         };
-        // ---- P^T = exp2(S^T c - m c) rounded to bf16, as the B operands of two 16-key P.V steps
-        auto exp_block = [&](const f32x16& s, float mc, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        // ---- P^T = exp2(S^T c - m c) rounded to bf16 for score pairs [lo, hi) of a block; pair i
+        //      (scores 2i, 2i+1) is word i % 4 of the B operand of 16-key P.V step i / 4
+        using PWords = uint32_t[8];
+        auto exp_pairs = [&](const f32x16& s, PWords& pw, auto lo_c, auto hi_c) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uint32_t w[4];
+            for (int i = decltype(lo_c)::value; i < decltype(hi_c)::value; ++i)
+                pw[i] = pack_bf16x2(fast_exp2(fmaf(s[2 * i], c, -mc_run)), fast_exp2(fmaf(s[2 * i + 1], c, -mc_run)));
+        };
+        // ---- this lane's sum of the block's rounded P (the probabilities fed to P.V)
+        auto block_sum = [&](const PWords& pw) __attribute__((always_inline)) {
+            float a = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, -mc));
-                    const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, -mc));
-                    w[i] = pack_bf16x2(p0, p1);
+            for (int i = 0; i < 8; ++i) a = add_bf16_pair(pw[i], a);
+            return a;
+        };
+        // ---- a block u whose exponentials ran against the reference max: if any lane's sum
+        //      exceeds the limit (some probability above 2^8, or a row without a reference yet),
+        //      move the reference to the block's max and redo its exponentials; then add the sum
+        //      to l.  The narrow heads settle a block while its scores are still live.  The wide
+        //      heads settle it after its scores have died (they die as the exponentials consume
+        //      them, which keeps them within 256 VGPRs): this rare path recomputes them from K in
+        //      global memory, whose LDS slot may already hold a later tile, every lane loading its
+        //      own fragments, bounded by the slice like the DMA, for the same MFMAs.
+        auto redo = [&](const f32x16& s, PWords& pw) __attribute__((always_inline)) {
+            rebase(s);
+            exp_pairs(s, pw, IC<0>{}, IC<8>{});
+            return block_sum(pw);
+        };
+        auto settle_live = [&](const f32x16& s, PWords& pw, float bs) __attribute__((always_inline)) {
+            if (__any(bs > lim)) bs = redo(s, pw);
+            l_run += bs;
+        };
+        const auto krs = make_rsrc(kbase, kslice);
+        auto settle_global = [&](int u, PWords& pw, float bs) __attribute__((always_inline)) {
+            if (__any(bs > lim)) {
+                const int key = u * 32 + col;
+                const uint32_t row = key < sk ? static_cast<uint32_t>(key * p.kv.ss * 2) : kOutOfRange;
+                f32x16 st = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) {
+                    const uint32_t off = row == kOutOfRange ? kOutOfRange : row + (kk * 16 + half * 8) * 2;
+                    const auto a = __builtin_bit_cast(bf16x8, buffer_load_b128(krs, off));
+                    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st, 0, 0, 0);
                 }
-                pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                if (need_mask(u)) mask_block(u, st);
+                bs = redo(st, pw);
             }
-        };
-        // ---- row sum of the rounded P fed to P.V
-        auto row_sum = [&](const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) l_run = add_bf16_pair(w[i], l_run);
-            }
+            l_run += bs;
         };
         // ---- O^T += V^T P^T over the 32-key block kb of a V tile: the A operand (32 channels x
         //      16 keys) comes from two transposing reads of row-major V; keys ks*16 +
         //      {half*4 .. +3} and {8 + half*4 .. +3} match the key order of P^T's B operand
-        auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+        auto pv_block = [&](const uint8_t* vl, int kb, const PWords& pw) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                const auto b = __builtin_bit_cast(bf16x8, u32x4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
 #pragma unroll
                 for (int cb = 0; cb < CBLK; ++cb) {
                     u32x2 part[2];
@@ -433,119 +471,143 @@ next_item:
                         part[r] = lds_read_tr16_b64(vl + key * VROWB + chunk * 16 + (ch & 7) * 2);
                     }
                     const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, oacc[cb], 0, 0, 0);
                 }
             }
         };
 
+        // Score pairs of block u + 1 (of 8 per lane) whose exponentials run under block u's P.V
+        // MFMAs.  The wide heads run the rest, the block sum and its check under the S MFMAs of
+        // block u + 2, so that the VALU work splits between the regions about as their MFMAs do;
+        // the narrow heads (EARLY = 8) run all of it, sum included, under P.V and settle the block
+        // right after, so that its scores die before the next S MFMAs.
+        constexpr int EARLY = TileCfg<DQK, DV>::EARLY;
+        constexpr bool NARROW = EARLY == 8;
+        using Early = IC<EARLY>;
         // Instruction counts of the interleaved regions (per wave and 32-key block).
-        constexpr int EXP_VALU = 16 + 16 + 8;           // FMA + exp per score, one pack per pair
-        constexpr int PV_MFMA = 2 * CBLK;               // two transposing V reads per MFMA
-        constexpr int PV_VALU = 8 + 8 + 1;              // row-sum dot2 + next block's max chain
+        constexpr int VALU_A = NARROW ? 0 : 5 * (8 - EARLY) + 8;   // FMA + exp per score, pack per pair; sum
+        constexpr int PV_MFMA = 2 * CBLK;                          // two transposing V reads per MFMA
+        constexpr int VALU_B = 5 * EARLY + (NARROW ? 8 : 0);
         constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
         constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
         constexpr int WAIT_K0 = (VM_PROLOGUE & 15) | ((VM_PROLOGUE >> 4) << 14) | 0x0F70;
         static_assert(VM_PROLOGUE < 64, "vmcnt is 6 bits");
-        // region A: S of the next block (KSTEPS MFMAs, one K read each) under the exponentials
-        //           of the current block
-        auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, float mc,
-                            bf16x8 (&pf)[2], const KPre& pre) __attribute__((always_inline)) {
+        // region A: S of the next block (KSTEPS MFMAs, one K read each); for the wide heads also
+        //           the last exponentials of the current block and its sum, which it returns
+        auto region_a = [&](const uint8_t* kl, int kb, f32x16& sn, const f32x16& s, PWords& pw,
+                            const KPre& pre) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
             qk_block(kl, kb, sn, pre);
-            exp_block(s, mc, pf);
-            // keep the exponentials here: without a use inside the region the compiler would sink
-            // them to the P.V MFMAs that consume them
-            asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-            sched_region<KSTEPS, KSTEPS - KPRE, 0, 1, EXP_VALU, 0>(std::make_integer_sequence<int, KSTEPS>{});
+            float bs = 0.f;
+            if constexpr (!NARROW) {
+                exp_pairs(s, pw, Early{}, IC<8>{});
+                bs = block_sum(pw);
+                // keep the sum here: without a use inside the region the compiler would sink it
+                asm volatile("" ::"v"(bs));
+            }
+            sched_region<KSTEPS, KSTEPS - KPRE, 0, 1, VALU_A, 0>(std::make_integer_sequence<int, KSTEPS>{});
             __builtin_amdgcn_sched_barrier(0);
+            return bs;
         };
-        // region B: P.V of the current block under its row sum and the next block's lane max;
-        // with PRE, it also reads the first fragments of the next region A's K block
-        auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], const f32x16& sn,
+        // region B: P.V of the current block under the first exponentials of the next one (in
+        // pw_next; for the narrow heads all of them and their sum, which it returns); with PRE,
+        // it also reads the first fragments of the next region A's K block
+        auto region_b = [&](const uint8_t* vl, int kb, const PWords& pw, const f32x16& sn, PWords& pw_next,
                             auto vmem_c, auto pre_c, const uint8_t* kl_next, int kb_next,
                             KPre& pre) __attribute__((always_inline)) {
             constexpr int NPRE = decltype(pre_c)::value ? KPRE : 0;
-            pv_block(vl, kb, pf);
-            row_sum(pf);
-            const float mx = lane_max(sn);
+            pv_block(vl, kb, pw);
+            exp_pairs(sn, pw_next, IC<0>{}, Early{});
+            float bs = 0.f;
+            if constexpr (NARROW) {
+                bs = block_sum(pw_next);
+                asm volatile("" ::"v"(bs));
+            } else {
+                // keep the exponentials here: without a use inside the region the compiler would
+                // sink them to the region that consumes them
+#pragma unroll
+                for (int i = 0; i < EARLY; ++i) asm volatile("" ::"v"(pw_next[i]));
+            }
             if constexpr (NPRE > 0) k_prefetch(kl_next, kb_next, pre);
-            // keep the row sum here: without a use inside the region the compiler would sink it
-            // past the region's end, where nothing hides it
-            asm volatile("" ::"v"(l_run));
-            sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+            sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, VALU_B, decltype(vmem_c)::value>(
                 std::make_integer_sequence<int, PV_MFMA>{});
             __builtin_amdgcn_sched_barrier(0);
-            return mx;
+            return bs;
         };
 
-        // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks: block
-        //      u's exponentials run under the S MFMAs of block u+1, and block u's P.V under the
-        //      lane max of block u+1.  Tile t's K sits in k slot t%2 and its V in v slot t%2.
-        //      The barrier of iteration t (after the S MFMAs of its second block) guarantees
-        //      that every wave's part of V_t and K_{t+1} has landed and that no wave still reads
-        //      K_t or V_{t-1}: their slots then take K_{t+2} and V_{t+1}.
-        using NoVmem = std::integral_constant<int, 0>;
-        using DmaVmem = std::integral_constant<int, KDMA + VDMA>;
-        // a tile that is not the last: its two blocks and the S of the next tile's first block
+        // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks (block u's
+        //      probabilities are finished and checked in the region A that runs the S MFMAs of
+        //      block u+1 (wide heads) or in the region B before it (narrow heads); block u's P.V
+        //      runs in the region B after it).  Tile t's K sits in k slot t%2 and its V in v slot
+        //      t%2; even blocks keep their scores in s0 and probabilities in p0, odd ones in
+        //      s1 / p1.  The barrier of iteration t (after the S MFMAs of its second block)
+        //      guarantees that every wave's part of V_t and K_{t+1} has landed and that no wave
+        //      still reads K_t or V_{t-1}: their slots then take K_{t+2} and V_{t+1}.
+        using NoVmem = IC<0>;
+        using DmaVmem = IC<KDMA + VDMA>;
         using Pre = std::true_type;
         using NoPre = std::false_type;
-        auto iteration = [&](int t, auto par_c, f32x16& s, float& mx, KPre& pre) __attribute__((always_inline)) {
-            using Cur = std::integral_constant<int, decltype(par_c)::value>;
-            using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
-            f32x16 sn;
-            bf16x8 pf[2];
-            // block 2t (exponentials, P.V) with block 2t+1 (S, max)
-            float mc = softmax_update(mx);
-            region_a(k_slot(Cur{}), 1, sn, s, mc, pf, pre);
-            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        auto iteration = [&](int t, auto par_c, f32x16& s0, f32x16& s1, PWords& p0, PWords& p1, KPre& pre)
+                             __attribute__((always_inline)) {
+            using Cur = IC<decltype(par_c)::value>;
+            using Nxt = IC<decltype(par_c)::value ^ 1>;
+            // block 2t (s0, p0) with the S of block 2t+1 (into s1)
+            float bs = region_a(k_slot(Cur{}), 1, s1, s0, p0, pre);
+            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, s1);
+            if constexpr (!NARROW) settle_global(2 * t, p0, bs);
             __builtin_amdgcn_s_waitcnt(WAIT_VM0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
             issue_k(t + 2, k_slot(Cur{}));
             issue_v(t + 1, v_slot(Nxt{}));
-            mx = region_b(v_slot(Cur{}), 0, pf, sn, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
-            s = sn;
-            // block 2t+1 with block 2t+2 (the first block of the next tile)
-            mc = softmax_update(mx);
-            region_a(k_slot(Nxt{}), 0, sn, s, mc, pf, pre);
-            if (need_mask(2 * t + 2)) mask_block(2 * t + 2, sn);
+            bs = region_b(v_slot(Cur{}), 0, p0, s1, p1, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
+            if constexpr (NARROW) settle_live(s1, p1, bs);
+            // block 2t+1 (s1, p1) with the S of block 2t+2, the first block of the next tile (into s0)
+            bs = region_a(k_slot(Nxt{}), 0, s0, s1, p1, pre);
+            if (need_mask(2 * t + 2)) mask_block(2 * t + 2, s0);
+            if constexpr (!NARROW) settle_global(2 * t + 1, p1, bs);
             __builtin_amdgcn_sched_barrier(0);
             // the next region A (an iteration or the last tile) starts on block 1 of K_{t+1}
-            mx = region_b(v_slot(Cur{}), 1, pf, sn, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
-            s = sn;
+            bs = region_b(v_slot(Cur{}), 1, p1, s0, p0, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
+            if constexpr (NARROW) settle_live(s0, p0, bs);
         };
         // the last tile: its two blocks, nothing further to load
-        auto last = [&](int t, auto par_c, const f32x16& s0, float mx, KPre& pre) __attribute__((always_inline)) {
-            using Cur = std::integral_constant<int, decltype(par_c)::value>;
-            f32x16 sn;
-            bf16x8 pf[2];
-            float mc = softmax_update(mx);
-            region_a(k_slot(Cur{}), 1, sn, s0, mc, pf, pre);
-            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        auto last = [&](int t, auto par_c, const f32x16& s0, f32x16& s1, PWords& p0, PWords& p1, KPre& pre)
+                        __attribute__((always_inline)) {
+            using Cur = IC<decltype(par_c)::value>;
+            float bs = region_a(k_slot(Cur{}), 1, s1, s0, p0, pre);
+            if (need_mask(2 * t + 1)) mask_block(2 * t + 1, s1);
+            if constexpr (!NARROW) settle_global(2 * t, p0, bs);
             __builtin_amdgcn_s_waitcnt(WAIT_VM0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            mx = region_b(v_slot(Cur{}), 0, pf, sn, NoVmem{}, NoPre{}, nullptr, 0, pre);
-            mc = softmax_update(mx);
-            exp_block(sn, mc, pf);
-            row_sum(pf);
-            pv_block(v_slot(Cur{}), 1, pf);
+            bs = region_b(v_slot(Cur{}), 0, p0, s1, p1, NoVmem{}, NoPre{}, nullptr, 0, pre);
+            if constexpr (NARROW) {
+                settle_live(s1, p1, bs);
+            } else {
+                exp_pairs(s1, p1, Early{}, IC<8>{});
+                settle_live(s1, p1, block_sum(p1));
+            }
+            pv_block(v_slot(Cur{}), 1, p1);
         };
 
         if (ntiles > t0) {
-            using Zero = std::integral_constant<int, 0>;
-            using One = std::integral_constant<int, 1>;
+            using Zero = IC<0>;
+            using One = IC<1>;
             issue_k(t0, k_slot(Zero{}));
             issue_v(t0, v_slot(Zero{}));
             issue_k(t0 + 1, k_slot(One{}));
             __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_t0 has landed
             __syncthreads();
-            f32x16 s;
+            f32x16 s0, s1;
+            PWords p0, p1;
             KPre pre;
             k_prefetch(k_slot(Zero{}), 0, pre);
-            qk_block(k_slot(Zero{}), 0, s, pre);
-            if (need_mask(2 * t0)) mask_block(2 * t0, s);
-            float mx = lane_max(s);
+            qk_block(k_slot(Zero{}), 0, s0, pre);
+            if (need_mask(2 * t0)) mask_block(2 * t0, s0);
+            rebase(s0);                           // the row's first reference max
+            exp_pairs(s0, p0, IC<0>{}, Early{});
+            if constexpr (NARROW) l_run = block_sum(p0);
             k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_t0
             // Tiles up to `need` hold a key that some row of this wave sees; past them (the
             // diagonal tiles of the rows above, or right of a window) the wave only keeps the
@@ -558,19 +620,19 @@ next_item:
             const int e = min(need, ntiles - 1);   // tiles run through iteration()
             int t = t0;
             for (; t + 2 <= e; t += 2) {
-                iteration(t, Zero{}, s, mx, pre);
-                iteration(t + 1, One{}, s, mx, pre);
+                iteration(t, Zero{}, s0, s1, p0, p1, pre);
+                iteration(t + 1, One{}, s0, s1, p0, p1, pre);
             }
             const bool odd = t < e;
-            if (odd) iteration(t++, Zero{}, s, mx, pre);
+            if (odd) iteration(t++, Zero{}, s0, s1, p0, p1, pre);
             if (need == ntiles) {
-                if (odd) last(t, One{}, s, mx, pre);
-                else last(t, Zero{}, s, mx, pre);
+                if (odd) last(t, One{}, s0, s1, p0, p1, pre);
+                else last(t, Zero{}, s0, s1, p0, p1, pre);
             } else {
                 // tile t has parity (t - t0) & 1; the last tile issues no further DMA
                 auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {
-                    using Cur = std::integral_constant<int, decltype(par_c)::value>;
-                    using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+                    using Cur = IC<decltype(par_c)::value>;
+                    using Nxt = IC<decltype(par_c)::value ^ 1>;
                     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
                     __syncthreads();
                     if (u + 1 < ntiles) {

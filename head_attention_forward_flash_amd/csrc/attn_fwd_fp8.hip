@@ -56,7 +56,17 @@ __device__ __forceinline__ float max_halves(float x) {
 constexpr int BM = 128;          // query rows per workgroup = one Q scale block
 constexpr int BN = 64;           // keys per tile (half a K/V scale block)
 constexpr int NTHREADS = 256;
-constexpr float kRescaleThreshold = 8.0f;     // log2 units
+// A lane's sum of the 16 probabilities of a block it computed against the reference max: at most
+// this, each probability is at most 2^8 (the reference lags the row max by at most 8 in log2
+// units), otherwise the block takes a new reference.
+constexpr float kSumLimit = 256.0f;
+// Score pairs (of 8 per lane and block) of block u+1 whose exponentials run under the P.V MFMAs
+// of block u (see the main loop).
+#ifndef MHA_FP8_EARLY
+#define MHA_FP8_EARLY 5
+#endif
+constexpr int EARLY = MHA_FP8_EARLY;
+template <int N> using IC = std::integral_constant<int, N>;
 constexpr float kMinFactor = 1.17549435e-38f;   // FLT_MIN
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
@@ -76,7 +86,7 @@ template <int MFMAS, int DS_TOTAL, int DS_PRE, int DS_PER, int VALU, int VMEM, i
 __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     constexpr int DS_SLOTS = (DS_TOTAL - DS_PRE) / DS_PER;
     constexpr int VALU_PER = (VALU + MFMAS - 1) / MFMAS;
-    constexpr int VALU_SLOTS = (VALU + VALU_PER - 1) / VALU_PER;
+    constexpr int VALU_SLOTS = VALU_PER > 0 ? (VALU + VALU_PER - 1) / VALU_PER : 0;
     if constexpr (DS_PRE > 0) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PRE, 0);
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
@@ -250,9 +260,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     f32x16 oacc[CBLK];
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
-    float m_run = kNegInf;   // running max in scaled base-2 units, same in lane and lane^32
+    float m_run = kNegInf;   // reference max in scaled base-2 units, same in lane and lane^32
     float neg_m = 0.f;       // -m_run, or 0 while m_run = -inf
-    float grow_at = kNegInf; // m_run + threshold, or -inf while m_run = -inf
+    float lim = -1.f;        // largest block sum that keeps the reference: kSumLimit, or -1
+                             // while m_run = -inf (then every block takes a reference)
     float l_run = 0.f;
 
     const int kx = kswz(col);
@@ -332,52 +343,54 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         a = max3(a, s[7], s[15]);
         return max_halves(__builtin_fmaxf(a, b)) * c;
     };
-    // ---- online softmax update (lazy: the reference max moves only when it grows by more
-    //      than 2^8 in probability); returns the exponent bias -m + log2 scale_v.  A row grows
-    //      when its block max exceeds grow_at = m_run + threshold, which is -inf while m_run is:
-    //      a first finite max always grows, a row without a visible key yet does not.
-    auto softmax_update = [&](float mt, float log2_sv) __attribute__((always_inline)) {
-        if (__any(mt > grow_at)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
+    // ---- the reference max (scaled base-2 units): set from a block's scores, moving O and l
+    //      to the new reference.  Only the first block of a row and the rare blocks that fail the
+    //      check below come here.
+    auto rebase = [&](const f32x16& s, float c) __attribute__((always_inline)) {
+        const float m_new = fmaxf(m_run, row_max(s, c));
+        const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-            m_run = m_new;
-            neg_m = m_new == kNegInf ? 0.f : -m_new;
-            grow_at = m_new == kNegInf ? kNegInf : m_new + kRescaleThreshold;
-        }
-        return neg_m + log2_sv;
+        for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+        m_run = m_new;
+        neg_m = m_new == kNegInf ? 0.f : -m_new;
+        lim = m_new == kNegInf ? -1.f : kSumLimit;
     };
-    // ---- P'^T = exp2(S^T c + bias) rounded to bf16, as the B operands of two 16-key steps
-    auto exp_block = [&](const f32x16& s, float c, float bias, bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+    // ---- P'^T = exp2(S^T c - m + log2 scale_v) rounded to bf16 for score pairs [lo, hi) of a
+    //      block; pair i is word i % 4 of the B operand of 16-key P.V step i / 4
+    using PWords = uint32_t[8];
+    auto exp_pairs = [&](const f32x16& s, const TileScale& sc, PWords& pw, auto lo_c, auto hi_c)
+                         __attribute__((always_inline)) {
+        const float bias = neg_m + sc.log2_sv;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p0 = fast_exp2(fmaf(s[ks * 8 + 2 * i], c, bias));
-                const float p1 = fast_exp2(fmaf(s[ks * 8 + 2 * i + 1], c, bias));
-                w[i] = pack_bf16x2(p0, p1);
-            }
-            pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
+        for (int i = decltype(lo_c)::value; i < decltype(hi_c)::value; ++i)
+            pw[i] = pack_bf16x2(fast_exp2(fmaf(s[2 * i], sc.c, bias)), fast_exp2(fmaf(s[2 * i + 1], sc.c, bias)));
     };
-    // ---- row sum of the bf16 P' fed to P.V, back to unscaled probabilities
-    auto row_sum = [&](const bf16x8 (&pf)[2], float inv_sv) __attribute__((always_inline)) {
+    // ---- this lane's sum of the block's bf16 P' (the values fed to P.V)
+    auto block_sum = [&](const PWords& pw) __attribute__((always_inline)) {
         float a = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a = add_bf16_pair(w[i], a);
+        for (int i = 0; i < 8; ++i) a = add_bf16_pair(pw[i], a);
+        return a;
+    };
+    // ---- a block whose exponentials ran against the reference max: its sum of probabilities
+    //      (P' back to unscaled ones); above the limit on any lane (some probability above 2^8, or
+    //      a row without a reference yet) the block takes its own max as the reference and its
+    //      exponentials rerun.  Then the sum joins l.
+    auto settle = [&](const f32x16& s, const TileScale& sc, PWords& pw, float raw) __attribute__((always_inline)) {
+        float bs = raw * sc.inv_sv;
+        if (__any(bs > lim)) {
+            rebase(s, sc.c);
+            exp_pairs(s, sc, pw, IC<0>{}, IC<8>{});
+            bs = block_sum(pw) * sc.inv_sv;
         }
-        l_run = fmaf(a, inv_sv, l_run);
+        l_run += bs;
     };
     // ---- O^T += V^T P'^T over the 32-key block kb of a V tile (transposing reads)
-    auto pv_block = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+    auto pv_block = [&](const uint8_t* vl, int kb, const PWords& pw) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            const auto b = __builtin_bit_cast(bf16x8, u32x4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
 #pragma unroll
             for (int cb = 0; cb < CBLK; ++cb) {
                 u32x2 part[2];
@@ -387,69 +400,88 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
                     part[r] = lds_read_tr16_b64(vl + key0 * VROWB + voff[cb]);
                 }
                 const auto a = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[cb], 0, 0, 0);
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, oacc[cb], 0, 0, 0);
             }
         }
     };
 
-    constexpr int EXP_VALU = 16 + 16 + 8;
+    // Score pairs of block u + 1 (of 8 per lane) whose exponentials run under block u's P.V
+    // MFMAs; the rest and the block sum run under the S MFMAs of block u + 2, where the block is
+    // settled.  EARLY = 8 runs all of it, sum included, under P.V and settles the block right
+    // after.
+    constexpr bool NARROW = EARLY == 8;
+    using Early = IC<EARLY>;
+    constexpr int VALU_A = NARROW ? 0 : 5 * (8 - EARLY) + 8;
     constexpr int PV_MFMA = 2 * CBLK;
-    constexpr int PV_VALU = 8 + 8 + 5;
+    constexpr int VALU_B = 5 * EARLY + (NARROW ? 8 : 0);
     constexpr int WAIT_VM0 = 0x0F70;                // s_waitcnt vmcnt(0)
     constexpr int VM_PROLOGUE = VDMA + KDMA;        // V_0 and K_1 may still be in flight
     static_assert(VM_PROLOGUE < 16, "vmcnt immediate");
     constexpr int WAIT_K0 = VM_PROLOGUE | 0x0F70;
-    // region A: S of the next block (D/64 fp8 MFMAs, two K reads each) under the exponentials of the
-    //           current block
-    auto region_a = [&](const uint8_t* kl, int kb, uint32_t ke, f32x16& sn, const f32x16& s, float c, float bias,
-                        bf16x8 (&pf)[2], const KPre& pre) __attribute__((always_inline)) {
+    // region A: S of the next block (D/64 fp8 MFMAs, two K reads each); unless NARROW also the last
+    //           exponentials of the current block and its raw sum, which it returns
+    auto region_a = [&](const uint8_t* kl, int kb, uint32_t ke, f32x16& sn, const f32x16& s, const TileScale& sc,
+                        PWords& pw, const KPre& pre) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         qk_block(kl, kb, sn, ke, pre);
-        exp_block(s, c, bias, pf);
-        // keep the exponentials here: without a use inside the region the compiler would sink
-        // them to the P.V MFMAs that consume them
-        asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+        float raw = 0.f;
+        if constexpr (!NARROW) {
+            exp_pairs(s, sc, pw, Early{}, IC<8>{});
+            raw = block_sum(pw);
+            // keep the sum here: without a use inside the region the compiler would sink it
+            asm volatile("" ::"v"(raw));
+        }
         // the later k-steps' reads open the region, under the first MFMA
-        sched_region<KS, 2 * (KS - 1), 2 * (KS - 1), 1, EXP_VALU, 0>(std::make_integer_sequence<int, KS>{});
+        sched_region<KS, 2 * (KS - 1), 2 * (KS - 1), 1, VALU_A, 0>(std::make_integer_sequence<int, KS>{});
         __builtin_amdgcn_sched_barrier(0);
+        return raw;
     };
-    // region B: P.V of the current block under its row sum and the next block's row max; with PRE,
-    // it also reads the first k-step of the next region A's K block
-    auto region_b = [&](const uint8_t* vl, int kb, const bf16x8 (&pf)[2], float inv_sv, const f32x16& sn,
-                        float c_next, auto vmem_c, auto pre_c, const uint8_t* kl_next, int kb_next,
+    // region B: P.V of the current block under the first exponentials of the next one (NARROW: all
+    // of them and their raw sum, which it returns); with PRE, it also reads the first k-step of the
+    // next region A's K block
+    auto region_b = [&](const uint8_t* vl, int kb, const PWords& pw, const f32x16& sn, const TileScale& sc_n,
+                        PWords& pw_next, auto vmem_c, auto pre_c, const uint8_t* kl_next, int kb_next,
                         KPre& pre) __attribute__((always_inline)) {
         constexpr int NPRE = decltype(pre_c)::value ? 2 : 0;
-        pv_block(vl, kb, pf);
-        row_sum(pf, inv_sv);
-        const float mt = row_max(sn, c_next);
+        pv_block(vl, kb, pw);
+        exp_pairs(sn, sc_n, pw_next, IC<0>{}, Early{});
+        float raw = 0.f;
+        if constexpr (NARROW) {
+            raw = block_sum(pw_next);
+            asm volatile("" ::"v"(raw));
+        } else {
+            // keep the exponentials here: without a use inside the region the compiler would sink
+            // them to the region that consumes them
+#pragma unroll
+            for (int i = 0; i < EARLY; ++i) asm volatile("" ::"v"(pw_next[i]));
+        }
         if constexpr (NPRE > 0) k_prefetch(kl_next, kb_next, pre);
-        sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, PV_VALU, decltype(vmem_c)::value>(
+        sched_region<PV_MFMA, 2 * PV_MFMA + NPRE, 2 * CBLK, 2, VALU_B, decltype(vmem_c)::value>(
             std::make_integer_sequence<int, PV_MFMA>{});
         __builtin_amdgcn_sched_barrier(0);
-        return mt;
+        return raw;
     };
 
     // ---- main loop over 64-key tiles, software-pipelined over their 32-key blocks (as in the
-    //      bf16 kernel).  Tile t's K sits in k slot t%2 and its V in v slot t%2; the barrier
-    //      of iteration t guarantees that every wave's part of V_t and K_{t+1} has landed and
-    //      that no wave still reads K_t or V_{t-1}: their slots then take K_{t+2}, V_{t+1}.
-    using NoVmem = std::integral_constant<int, 0>;
-    using DmaVmem = std::integral_constant<int, KDMA + VDMA + (MX ? 2 : 0)>;
+    //      bf16 kernel).  Tile t's K sits in k slot t%2 and its V in v slot t%2; even blocks keep
+    //      their scores in s0 and probabilities in p0, odd ones in s1 / p1.  The barrier of
+    //      iteration t guarantees that every wave's part of V_t and K_{t+1} has landed and that no
+    //      wave still reads K_t or V_{t-1}: their slots then take K_{t+2}, V_{t+1}.
+    using NoVmem = IC<0>;
+    using DmaVmem = IC<KDMA + VDMA + (MX ? 2 : 0)>;
     // (MXFP8: ke[0] holds the exponent words of tile t, ke[1] those of tile t+1; the words of
     // tile t+2 are loaded with its K tile)
     using Pre = std::true_type;
     using NoPre = std::false_type;
-    auto iteration = [&](int t, auto par_c, f32x16& s, float& mt, TileScale& sc, u32x2 (&ke)[2], KPre& pre)
-                         __attribute__((always_inline)) {
-        using Cur = std::integral_constant<int, decltype(par_c)::value>;
-        using Nxt = std::integral_constant<int, decltype(par_c)::value ^ 1>;
+    auto iteration = [&](int t, auto par_c, f32x16& s0, f32x16& s1, PWords& p0, PWords& p1, TileScale& sc,
+                         u32x2 (&ke)[2], KPre& pre) __attribute__((always_inline)) {
+        using Cur = IC<decltype(par_c)::value>;
+        using Nxt = IC<decltype(par_c)::value ^ 1>;
         const TileScale sc_next = tile_scale(t + 1);
-        f32x16 sn;
-        bf16x8 pf[2];
-        // block 2t (exponentials, P.V) with block 2t+1 (S, max)
-        float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s, sc.c, bias, pf, pre);
-        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+        // block 2t (s0, p0) with the S of block 2t+1 (into s1)
+        float raw = region_a(k_slot(Cur{}), 1, ke[0][1], s1, s0, sc, p0, pre);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, s1);
+        if constexpr (!NARROW) settle(s0, sc, p0, raw);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
@@ -457,41 +489,42 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         if constexpr (MX) ke_new = kexp_load(t + 2);
         issue_k(t + 2, k_slot(Cur{}));
         issue_v(t + 1, v_slot(Nxt{}));
-        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
-        // block 2t+1 (now in sn) with block 2t+2 (the first block of the next tile), whose S goes
-        // into s: the two score buffers swap roles instead of being copied
-        bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Nxt{}), 0, ke[1][0], s, sn, sc.c, bias, pf, pre);
-        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, s);
+        raw = region_b(v_slot(Cur{}), 0, p0, s1, sc, p1, DmaVmem{}, Pre{}, k_slot(Nxt{}), 0, pre);
+        if constexpr (NARROW) settle(s1, sc, p1, raw);
+        // block 2t+1 (s1, p1) with the S of block 2t+2, the first block of the next tile (into s0)
+        raw = region_a(k_slot(Nxt{}), 0, ke[1][0], s0, s1, sc, p1, pre);
+        if (need_mask(2 * t + 2)) mask_block(2 * t + 2, s0);
+        if constexpr (!NARROW) settle(s1, sc, p1, raw);
         __builtin_amdgcn_sched_barrier(0);
         // the next region A (an iteration or the last tile) starts on block 1 of K_{t+1}
-        mt = region_b(v_slot(Cur{}), 1, pf, sc.inv_sv, s, sc_next.c, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
+        raw = region_b(v_slot(Cur{}), 1, p1, s0, sc_next, p0, NoVmem{}, Pre{}, k_slot(Nxt{}), 1, pre);
+        if constexpr (NARROW) settle(s0, sc_next, p0, raw);
         sc = sc_next;
         ke[0] = ke[1];
         ke[1] = ke_new;
     };
     // the last tile: its two blocks, nothing further to load
-    auto last = [&](int t, auto par_c, const f32x16& s0, float mt, const TileScale& sc, const u32x2 (&ke)[2],
-                    KPre& pre) __attribute__((always_inline)) {
-        using Cur = std::integral_constant<int, decltype(par_c)::value>;
-        f32x16 sn;
-        bf16x8 pf[2];
-        float bias = softmax_update(mt, sc.log2_sv);
-        region_a(k_slot(Cur{}), 1, ke[0][1], sn, s0, sc.c, bias, pf, pre);
-        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, sn);
+    auto last = [&](int t, auto par_c, const f32x16& s0, f32x16& s1, PWords& p0, PWords& p1, const TileScale& sc,
+                    const u32x2 (&ke)[2], KPre& pre) __attribute__((always_inline)) {
+        using Cur = IC<decltype(par_c)::value>;
+        float raw = region_a(k_slot(Cur{}), 1, ke[0][1], s1, s0, sc, p0, pre);
+        if (need_mask(2 * t + 1)) mask_block(2 * t + 1, s1);
+        if constexpr (!NARROW) settle(s0, sc, p0, raw);
         __builtin_amdgcn_s_waitcnt(WAIT_VM0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        mt = region_b(v_slot(Cur{}), 0, pf, sc.inv_sv, sn, sc.c, NoVmem{}, NoPre{}, nullptr, 0, pre);
-        bias = softmax_update(mt, sc.log2_sv);
-        exp_block(sn, sc.c, bias, pf);
-        row_sum(pf, sc.inv_sv);
-        pv_block(v_slot(Cur{}), 1, pf);
+        raw = region_b(v_slot(Cur{}), 0, p0, s1, sc, p1, NoVmem{}, NoPre{}, nullptr, 0, pre);
+        if constexpr (!NARROW) {
+            exp_pairs(s1, sc, p1, Early{}, IC<8>{});
+            raw = block_sum(p1);
+        }
+        settle(s1, sc, p1, raw);
+        pv_block(v_slot(Cur{}), 1, p1);
     };
 
     if (ntiles > 0) {
-        using Zero = std::integral_constant<int, 0>;
-        using One = std::integral_constant<int, 1>;
+        using Zero = IC<0>;
+        using One = IC<1>;
         u32x2 ke[2] = {{0u, 0u}, {0u, 0u}};
         if constexpr (MX) {   // issued before the DMA, so the wait below covers them too
             ke[0] = kexp_load(0);
@@ -503,23 +536,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
         __syncthreads();
         TileScale sc = tile_scale(0);
-        f32x16 s;
+        f32x16 s0, s1;
+        PWords p0, p1;
         KPre pre;
         k_prefetch(k_slot(Zero{}), 0, pre);
-        qk_block(k_slot(Zero{}), 0, s, ke[0][0], pre);
-        if (need_mask(0)) mask_block(0, s);
-        float mt = row_max(s, sc.c);
+        qk_block(k_slot(Zero{}), 0, s0, ke[0][0], pre);
+        if (need_mask(0)) mask_block(0, s0);
+        rebase(s0, sc.c);                     // the row's first reference max
+        exp_pairs(s0, sc, p0, IC<0>{}, Early{});
+        if constexpr (NARROW) l_run = block_sum(p0) * sc.inv_sv;
         k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_0
         int t = 0;
         for (; t + 2 < ntiles; t += 2) {
-            iteration(t, Zero{}, s, mt, sc, ke, pre);
-            iteration(t + 1, One{}, s, mt, sc, ke, pre);
+            iteration(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
+            iteration(t + 1, One{}, s0, s1, p0, p1, sc, ke, pre);
         }
         if (t + 1 < ntiles) {
-            iteration(t, Zero{}, s, mt, sc, ke, pre);
-            last(t + 1, One{}, s, mt, sc, ke, pre);
+            iteration(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
+            last(t + 1, One{}, s0, s1, p0, p1, sc, ke, pre);
         } else {
-            last(t, Zero{}, s, mt, sc, ke, pre);
+            last(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
         }
     }
 

@@ -20,6 +20,7 @@ workload, on all BLAS threads and on one.
 Prints ONE JSON line.  Other modes:
     python bench.py --calibrate-copy BYTES        a plain device copy of BYTES (counter scaling)
     python bench.py --summarize-trace CSV [RE]    per-kernel statistics of a rocprofv3 kernel trace
+    python bench.py --summarize-counters CSV...   per-kernel counters of rocprofv3 --pmc passes
     python bench.py --fp8-only / --varlen-workload NAME / --workload NAME --configs none
 """
 
@@ -324,7 +325,8 @@ def bench_varlen(dev, name, n, warmup):
 
 
 def summarize_trace(path, pattern=None):
-    """Per-kernel statistics of a rocprofv3 kernel trace (CSV): calls, mean, the chronological
+    """Per-kernel statistics of a rocprofv3 kernel trace (CSV), one row per (kernel, grid size)
+    (so that workloads sharing a kernel instance stay apart): calls, mean, the chronological
     middle-80 % trimmed mean, median and max, plus the registers and LDS of the code object."""
     import csv
     rows = {}
@@ -333,15 +335,77 @@ def summarize_trace(path, pattern=None):
             name = r["Kernel_Name"]
             if pattern and not re.search(pattern, name):
                 continue
-            d = rows.setdefault(name, {"t": [], "meta": r})
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            d = rows.setdefault((name, grid // max(wg, 1)), {"t": [], "meta": r})
             d["t"].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-    print("| kernel | calls | mean us | trimmed mean us (middle 80 %) | median us | max us | VGPR | AGPR | SGPR | LDS B |")
-    print("|---|---|---|---|---|---|---|---|---|---|")
-    for name, d in rows.items():
+    print("| kernel | workgroups | calls | mean us | trimmed mean us (middle 80 %) | median us | max us "
+          "| VGPR | AGPR | SGPR | LDS B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for (name, nwg), d in rows.items():
         st = trimmed_stats([t for _, t in sorted(d["t"])])
         m = d["meta"]
-        print(f"| `{name}` | {st['n']} | {st['mean_us']} | {st['trimmed_mean_us']} | {st['median_us']} | {st['max_us']} "
-              f"| {m.get('VGPR_Count')} | {m.get('Accum_VGPR_Count')} | {m.get('SGPR_Count')} | {m.get('LDS_Block_Size')} |")
+        print(f"| `{name}` | {nwg} | {st['n']} | {st['mean_us']} | {st['trimmed_mean_us']} | {st['median_us']} "
+              f"| {st['max_us']} | {m.get('VGPR_Count')} | {m.get('Accum_VGPR_Count')} | {m.get('SGPR_Count')} "
+              f"| {m.get('LDS_Block_Size')} |")
+
+
+def summarize_counters(paths, pattern=None, simds=1024, xcds=8):
+    """Mean per dispatch of every counter in rocprofv3 --pmc CSVs (one or more passes), per
+    (kernel, grid size), and the derived figures: core clock, matrix-pipe busy fraction per
+    SIMD, VALU-active and waiting fractions of wave time, instructions per MFMA, LDS bank
+    conflicts.  GRBM_GUI_ACTIVE sums the XCDs' busy cycles; SQ_VALU_MFMA_BUSY_CYCLES sums the
+    SIMDs'; SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_* count quad-cycles per wave;
+    SQ_INSTS_VALU includes the MFMAs."""
+    import csv
+    import statistics
+    acc = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if pattern and not re.search(pattern, name):
+                    continue
+                d = acc.setdefault((name, int(r["Grid_Size"])), {"c": {}, "dur": {}})
+                d["c"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                key = (path, r["Dispatch_Id"])
+                d["dur"][key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    for (name, grid), d in acc.items():
+        c = {k: sum(v) / len(v) for k, v in d["c"].items()}
+        n = min(len(v) for v in d["c"].values())
+        dur = statistics.median(d["dur"].values())
+        print(f"### `{name}`, grid {grid} threads\n")
+        print(f"Dispatches averaged: {n} or more per counter; median dispatch {dur:.1f} us.\n")
+        print("| counter | mean per dispatch |\n|---|---|")
+        for k in sorted(c):
+            print(f"| {k} | {c[k]:.4g} |")
+        print()
+        g = c.get("GRBM_GUI_ACTIVE")
+        if g:
+            cyc = g / xcds
+            print(f"* core clock: {cyc / dur / 1e3:.2f} GHz ({cyc:.4g} cycles per XCD)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                print(f"* matrix pipe busy: {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * cyc):.1f}% of cycles per SIMD")
+        wc = c.get("SQ_WAVE_CYCLES")
+        if wc:
+            for k, label in (("SQ_ACTIVE_INST_VALU", "VALU active"), ("SQ_ACTIVE_INST_LDS", "LDS active"),
+                             ("SQ_WAIT_INST_ANY", "waiting at s_waitcnt / dependencies")):
+                if k in c:
+                    print(f"* {label}: {100 * c[k] / wc:.1f}% of wave time")
+        mf = c.get("SQ_INSTS_MFMA")
+        if mf:
+            for k, label in (("SQ_INSTS_VALU", "VALU (besides the MFMAs)"), ("SQ_INSTS_VALU_TRANS_F32", "of them exp"),
+                             ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_SALU", "SALU")):
+                if k in c:
+                    v = c[k] - mf if k == "SQ_INSTS_VALU" else c[k]
+                    print(f"* {label}: {v / mf:.2f} per MFMA")
+        if c.get("SQ_LDS_IDX_ACTIVE"):
+            print(f"* LDS bank conflicts: {c.get('SQ_LDS_BANK_CONFLICT', 0):.4g} cycles "
+                  f"({100 * c.get('SQ_LDS_BANK_CONFLICT', 0) / c['SQ_LDS_IDX_ACTIVE']:.2f}% of LDS-active cycles)")
+        for k in ("FETCH_SIZE", "WRITE_SIZE"):
+            if k in c:
+                print(f"* {k}: {c[k]:.6g} KiB per dispatch")
+        print()
 
 
 def main():
@@ -360,12 +424,18 @@ def main():
     ap.add_argument("--varlen-workload", default=None, help="time only this packed-sequence workload; print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-trace", nargs="+", metavar=("CSV", "REGEX"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="rocprofv3 --pmc counter CSVs (one per pass); --kernel-regex filters")
+    ap.add_argument("--kernel-regex", default=None)
     a = ap.parse_args()
     if a.no_fp8:
         a.configs = "none"
 
     if a.summarize_trace:
         summarize_trace(a.summarize_trace[0], a.summarize_trace[1] if len(a.summarize_trace) > 1 else None)
+        return
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters, a.kernel_regex)
         return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -6,8 +6,8 @@
 // dqk=192/dv=128 "pe" bucket; Profile 2: pipelining depth as the main lever).
 //
 // Work decomposition: one workgroup per (batch, query head, block of BM query
-// rows), one wave per 32 rows; causal grids that fill the device only a few
-// times give each workgroup the pair of blocks j and n-1-j instead.  The kernel computes the TRANSPOSED scores
+// rows), one wave per 32 rows; causal grids give each workgroup the pair of
+// blocks j and n-1-j instead (packed sequences only on short grids).  The kernel computes the TRANSPOSED scores
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds one query row
 // (lane % 32) and half of the keys of each 32-key block: the row max and row sum
 // stay in the lane except for one exchange with lane ^ 32, and the probabilities
@@ -693,9 +693,11 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     p.n_mblocks = (p.sq + BM - 1) / BM;
     const int64_t blocks = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
     if (blocks == 0) return hipSuccess;
-    // Pair causal query blocks when the grid fills the device a few times at most; on longer
-    // grids the hardware's dispatch already overlaps short and long workgroups (measured:
-    // pairing gains 5-10% on 2-8 rounds, nothing on 16).
+    // Pair causal query blocks, so that every workgroup does the same work and the in-order
+    // dispatch never waits behind a long one (measured: -5 to -10% on grids of 2-8 rounds of
+    // resident workgroups, -1.7% on the 16-round MLA grid, -2.6% on d128 8192^2 hq128).  Packed
+    // sequences pair only on grids of at most 8 rounds: their workgroups are dealt to the XCDs
+    // by (sequence, kv head), and pairing the 32-sequence workload's 8192-row grid cost +11%.
     const bool ext = p.window_left >= 0 || (!CAUSAL && p.window_right >= 0) || p.sinks != nullptr;
     if (ext) {
         if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
@@ -703,8 +705,8 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
                            dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0, stream, p);
         return hipGetLastError();
     }
-    bool paired = false;
-    if (CAUSAL && p.n_mblocks > 1) {
+    bool paired = CAUSAL && p.n_mblocks > 1;
+    if (paired && VARLEN) {
         int groups = 0;
         const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false>;
         const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2, &groups);

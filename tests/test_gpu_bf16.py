@@ -241,3 +241,24 @@ def test_running_max_rising_in_steps(dims):
             for causal in (False, True):
                 _check_all(q, k, v, causal, f"d{dqk} ramp rising={rising} scale={scale} causal={causal}",
                            scale=scale)
+
+
+@pytest.mark.parametrize("dims", [(32, 32), (64, 64), (128, 128), (192, 128)])
+def test_late_score_spike_overflows_the_reference(dims):
+    # One key late in the sequence scores ~150 (natural-log units) above every other key, for every
+    # query: against the reference max taken from the first block its probability overflows fp32
+    # (2^216), so the block must take the rare path that moves the reference (for d128/d192 after
+    # recomputing the block's scores from K in global memory) and redo its exponentials.  Keys
+    # before the spike keep their tiny weights relative to it.
+    dqk, dv = dims
+    s = 300
+    q = workloads.make_random((1, s, 2, dqk), 8100 + dqk, dtype=torch.float32, std=0.1)
+    k = workloads.make_random((1, s, 2, dqk), 8101 + dqk, dtype=torch.float32, std=0.1)
+    q[..., 0] = 1.0
+    for spike in (257, 100):
+        k2 = k.clone()
+        k2[0, spike, :, 0] = 150.0 * dqk ** 0.5
+        v = workloads.make_random((1, s, 2, dv), 8102 + dqk)
+        for causal in (False, True):
+            _check_all(q.to(torch.bfloat16), k2.to(torch.bfloat16), v, causal,
+                       f"d{dqk} spike at key {spike} causal={causal}")

@@ -183,3 +183,17 @@ def test_running_max_rising_in_steps(q0):
     q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
     for causal in (False, True):
         _check_attention(q, k, v, _oracle_mu(k), causal, f"ramp q0={q0} causal={causal}")
+
+
+def test_late_score_spike_overflows_the_reference():
+    # As the bf16 test of the same name: one late key scores ~150 above the rest, so the fp8
+    # kernel's speculative exponentials overflow and the block takes a new reference.
+    d, s = 128, 384
+    q = workloads.make_random((1, s, 2, d), 8200, dtype=torch.float32, std=0.1)
+    k = workloads.make_random((1, s, 2, d), 8201, dtype=torch.float32, std=0.1)
+    q[..., 0] = 1.0
+    k[0, 300, :, 0] = 150.0 * d ** 0.5
+    v = workloads.make_random((1, s, 2, d), 8202)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    for causal in (False, True):
+        _check_attention(q, k, v, None, causal, f"spike causal={causal}")

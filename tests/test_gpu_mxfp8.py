@@ -144,3 +144,15 @@ def test_mxfp8_deterministic():
     a = _call(q, k, v, mu, True)
     b = _call(q, k, v, mu, True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_late_score_spike_overflows_the_reference():
+    d, s = 128, 384
+    q = workloads.make_random((1, s, 2, d), 8300, dtype=torch.float32, std=0.1)
+    k = workloads.make_random((1, s, 2, d), 8301, dtype=torch.float32, std=0.1)
+    q[..., 0] = 1.0
+    k[0, 300, :, 0] = 150.0 * d ** 0.5
+    v = workloads.make_random((1, s, 2, d), 8302)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    for causal in (False, True):
+        _check(q, k, v, None, causal, f"spike causal={causal}")

@@ -205,6 +205,7 @@ def oracle_timing(w, q, k, v, budget_s, budget_1core_s):
 
 
 def _bf16_step(w, q, k, v, o):
+    import torch
     import head_attention_forward_flash_amd as mha
     import workloads
     sinks = workloads.make_sinks(w)
@@ -215,8 +216,16 @@ def _bf16_step(w, q, k, v, o):
             mha.mha_fwd_bf16_window_sink(q, k, v, causal=w.causal, window_left=w.window_left,
                                          window_right=w.window_right, sinks=sinks_d, softmax_scale=w.scale, out=o)
     else:
+        # the key-range split's plan and workspace are set up once, outside the timed calls
+        n_split = mha.mha_fwd_bf16_split_plan(w.b, w.hq, w.hk, w.sq, w.sk, w.d_qk, w.d_v, w.causal)
+        ws = None
+        if n_split > 1:
+            ws = torch.empty(mha.mha_fwd_bf16_split_workspace_bytes(w.b, w.hq, w.sq, w.d_qk, w.d_v, n_split),
+                             dtype=torch.uint8, device=q.device)
+
         def step():
-            mha.mha_fwd_bf16(q, k, v, causal=w.causal, softmax_scale=w.scale, out=o)
+            mha.mha_fwd_bf16(q, k, v, causal=w.causal, softmax_scale=w.scale, out=o, n_split=n_split, workspace=ws)
+        step.n_split = n_split
     return step
 
 
@@ -234,8 +243,14 @@ def bench_bf16(w, dev, n, warmup, oracle_budget=None, tiny=False):
     q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
     o = torch.empty((w.b, w.sq, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-    st = time_dispatches(_bf16_step(w, q, k, v, o), stream, n, warmup)
+    step = _bf16_step(w, q, k, v, o)
+    st = time_dispatches(step, stream, n, warmup)
     out = {"workload": w.name, "shape": w.description, "kernel": "attn_fwd_bf16", "dispatch_us": st}
+    if getattr(step, "n_split", 1) > 1:
+        out["n_split"] = step.n_split
+        out["kernel"] = "attn_fwd_bf16 (key ranges) + attn_split_merge"
+        out["note"] = "each query block's keys in n_split ranges, merged by a second kernel; timed as one call"
+    del step
     if tiny:
         out["note"] = "launch-latency bound (8.4 MFLOP): reported in us only"
     else:

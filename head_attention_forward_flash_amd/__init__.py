@@ -6,7 +6,8 @@ and the current stream only.  There is no fallback: if libmha.so is missing or
 the tensors are not on a ROCm device the calls raise.
 
 Entry points (same names as the C ABI):
-    mha_fwd_bf16(q, k, v, causal=False, softmax_scale=None, out=None, lse=True)
+    mha_fwd_bf16(q, k, v, causal=False, softmax_scale=None, out=None, lse=True, n_split=None, workspace=None)
+    mha_fwd_bf16_split_plan(b, hq, hk, sq, sk, d_qk, d_v, causal) -> n_split
     mha_fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False, ...)
     k_smooth_mean(k, key_stride=1, max_keys=0, tau=0.25)
     mha_fwd_fp8(q, k, v, k_mean=None, causal=False, softmax_scale=None, out=None, lse=True)
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "k_smooth_mean_workspace_bytes", "k_smooth_mean", "mha_fwd_fp8_workspace_bytes",
     "mha_fp8_workspace_layout", "mha_fwd_fp8", "mha_fwd_mxfp8_workspace_bytes", "mha_mxfp8_workspace_layout",
     "mha_fwd_mxfp8", "mha_status_string", "mha_last_error", "mha_debug_sync_enabled", "k_smooth_mean_noalloc",
+    "mha_fwd_bf16_split", "mha_fwd_bf16_split_workspace_bytes", "mha_fwd_bf16_split_plan",
 )
 
 
@@ -64,6 +66,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mha_fwd_bf16.restype = i32
     lib.mha_fwd_bf16.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
                                  i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.mha_fwd_bf16_split.restype = i32
+    lib.mha_fwd_bf16_split.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp,
+                                       i32, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.mha_fwd_bf16_split_workspace_bytes.restype = sz
+    lib.mha_fwd_bf16_split_workspace_bytes.argtypes = [i32] * 6
+    lib.mha_fwd_bf16_split_plan.restype = i32
+    lib.mha_fwd_bf16_split_plan.argtypes = [i32] * 8 + [ctypes.POINTER(i32)]
     lib.mha_fwd_bf16_varlen.restype = i32
     lib.mha_fwd_bf16_varlen.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, vp, vp, vp,
                                         i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -187,9 +196,26 @@ def _attn_shapes(q, k, v, out, ndim):
     return qs, ks, d_v
 
 
+def mha_fwd_bf16_split_workspace_bytes(b: int, hq: int, sq: int, d_qk: int, d_v: int, n_split: int) -> int:
+    """Workspace bytes of mha_fwd_bf16 with n_split key ranges (0 for n_split <= 1)."""
+    return int(load_library().mha_fwd_bf16_split_workspace_bytes(b, hq, sq, d_qk, d_v, n_split))
+
+
+def mha_fwd_bf16_split_plan(b: int, hq: int, hk: int, sq: int, sk: int, d_qk: int, d_v: int,
+                            causal: bool = False) -> int:
+    """Key ranges per query block that balance this shape's grid on the current device (1: none)."""
+    n = ctypes.c_int(1)
+    _check(load_library().mha_fwd_bf16_split_plan(b, hq, hk, sq, sk, d_qk, d_v, int(bool(causal)), ctypes.byref(n)))
+    return n.value
+
+
 def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, out=None,
-                 lse: bool = True):
-    """Fused attention forward in bf16. Returns (o, lse) with lse [b, hq, sq] fp32 (or None)."""
+                 lse: bool = True, n_split: Optional[int] = None, workspace=None):
+    """Fused attention forward in bf16. Returns (o, lse) with lse [b, hq, sq] fp32 (or None).
+
+    n_split: key ranges per query block (mha_fwd_bf16_split); None asks the library for the
+    split that balances the grid on q's device.  A split needs a workspace: `workspace`
+    (contiguous uint8 on q's device) or one allocated here."""
     torch = _torch()
     lib = load_library()
     (b, sq, hq, d_qk), (_, sk, hk, _), d_v = _attn_shapes(q, k, v, out, 4)
@@ -199,9 +225,22 @@ def mha_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: Optional[float] =
     if out is None:
         out = torch.empty((b, sq, hq, d_v), dtype=torch.bfloat16, device=q.device)
     lse_t = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse else None
-    _check(lib.mha_fwd_bf16(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
-                            _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
-                            float(softmax_scale), int(bool(causal)), _stream(q.device)))
+    if n_split is None:
+        with torch.cuda.device(q.device):
+            n_split = mha_fwd_bf16_split_plan(b, hq, hk, sq, sk, d_qk, d_v, causal)
+    if n_split == 1:
+        _check(lib.mha_fwd_bf16(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
+                                _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
+                                float(softmax_scale), int(bool(causal)), _stream(q.device)))
+        return out, lse_t
+    need = mha_fwd_bf16_split_workspace_bytes(b, hq, sq, d_qk, d_v, int(n_split))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace("workspace", workspace, need, q.device)
+    _check(lib.mha_fwd_bf16_split(_ptr(q), _bshd_strides(q), _ptr(k), _bshd_strides(k), _ptr(v), _bshd_strides(v),
+                                  _ptr(out), _bshd_strides(out), _ptr(lse_t), b, hq, hk, sq, sk, d_qk, d_v,
+                                  float(softmax_scale), int(bool(causal)), int(n_split), _ptr(workspace),
+                                  workspace.numel(), _stream(q.device)))
     return out, lse_t
 
 

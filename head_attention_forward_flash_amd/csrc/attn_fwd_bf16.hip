@@ -85,7 +85,8 @@ template <int MFMAS, int DS_TOTAL, int DS_PRE, int DS_PER, int VALU, int VMEM, i
 __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     constexpr int DS_SLOTS = (DS_TOTAL - DS_PRE) / DS_PER;
     constexpr int VALU_PER = (VALU + MFMAS - 1) / MFMAS;
-    constexpr int VALU_SLOTS = VALU_PER > 0 ? (VALU + VALU_PER - 1) / VALU_PER : 0;
+    constexpr int VALU_DIV = VALU_PER > 0 ? VALU_PER : 1;
+    constexpr int VALU_SLOTS = VALU_PER > 0 ? (VALU + VALU_DIV - 1) / VALU_DIV : 0;
     if constexpr (DS_PRE > 0) __builtin_amdgcn_sched_group_barrier(kGrpDsRead, DS_PRE, 0);
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
@@ -108,8 +109,10 @@ template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, E
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, EARLY = MHA_EARLY_WIDE; };
 
 // EXT: sliding window (keys j with i - window_left <= j <= i + window_right, positions inside
-// the sequence) and per-head sink logits.
-template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT>
+// the sequence) and per-head sink logits.  SPLIT: p.n_split workgroups per query block, each over
+// one contiguous range of key tiles (dense, non-causal grids that would underfill the device),
+// leaving partial states for attn_split_merge.
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
     constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
@@ -148,6 +151,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     //      the same work and the grid has no tail of light workgroups.
     static_assert(CAUSAL || !PAIRED, "only causal blocks differ in work");
     static_assert(!EXT || !PAIRED, "windows and sinks run on unpaired grids");
+    static_assert(!SPLIT || (!CAUSAL && !VARLEN && !EXT), "the key split runs on dense, non-causal grids");
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
@@ -167,6 +171,10 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
             lid = pid;
         }
     }
+    // SPLIT: the key ranges of one query block are consecutive ids (one XCD), range fastest
+    const int split = SPLIT ? lid % p.n_split : 0;
+    if constexpr (SPLIT) lid /= p.n_split;
+    [[maybe_unused]] const int item = lid;    // (batch, head, query block) of this workgroup
     const int mrev = lid % per_head;
     const int bh = lid / per_head;
     int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first
@@ -243,6 +251,18 @@ next_item:
         if constexpr (EXT) {
             if (!CAUSAL && p.window_right >= 0) kv_end = min(sk, (mblk + 1) * BM + p.window_right);
             if (p.window_left >= 0) t0 = max(0, mblk * BM - p.window_left) / BN;
+        }
+        if constexpr (SPLIT) {
+            // key tiles [t0, t1) of the ceil(sk / BN); the ranges differ by at most one tile.  The
+            // K and V slices end at the range, so the DMA that runs ahead of the last tile reads
+            // nothing past it.
+            const int nt = (sk + BN - 1) / BN;
+            t0 = split * nt / p.n_split;
+            kv_end = min(sk, (split + 1) * nt / p.n_split * BN);
+            if (kv_end < sk) {
+                kslice = static_cast<uint32_t>((static_cast<int64_t>(kv_end - 1) * p.kv.ss + DQK) * 2);
+                vslice = static_cast<uint32_t>((static_cast<int64_t>(kv_end - 1) * p.vv.ss + DV) * 2);
+            }
         }
         const int ntiles = (kv_end + BN - 1) / BN;
 
@@ -653,6 +673,23 @@ next_item:
         float l_tot = l_run + swap_halves(l_run);
         float m_log2 = m_run * c;   // the reference max in base-2 units (c > 0 keeps -inf)
         float o_scale = 1.f;
+        if constexpr (SPLIT) {
+            // this key range's state goes to the workspace and the merge kernel finishes the row:
+            // O unnormalised, in accumulator order (the merge reads it back lane for lane), and
+            // per lane the base-2 reference max and the row sum
+            const int64_t slot = (static_cast<int64_t>(item) * p.n_split + split) * NWAVES + wave;
+            float* po = p.split_o + slot * (CBLK * 16 * 64);
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 w = {oacc[cb][4 * q4], oacc[cb][4 * q4 + 1], oacc[cb][4 * q4 + 2], oacc[cb][4 * q4 + 3]};
+                    *reinterpret_cast<f32x4*>(po + ((cb * 4 + q4) * 64 + lane) * 4) = w;
+                }
+            }
+            reinterpret_cast<f32x2*>(p.split_ml)[slot * 64 + lane] = f32x2{m_log2, l_tot};
+            return;
+        }
         if constexpr (EXT) {
             // the head's sink logit joins the normaliser: rebase both terms on their larger
             // exponent so that neither overflows
@@ -687,6 +724,63 @@ item_done: __attribute__((unused));
     }
 }
 
+// The key-range split's second kernel: one workgroup per query block, laid out like the
+// attention kernel's (one wave per 32 rows, the same lanes), merges the n_split partial states in
+// ascending order of key range.  The softmax over the union of the ranges is
+//   O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,   M = max_i m_i   (base-2 units),
+// and LSE = (M + log2 of the denominator) ln 2, so the result does not depend on timing.
+template <int DQK, int DV>
+__global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2)) void attn_split_merge(const AttnParams p) {
+    constexpr int BM = TileCfg<DQK, DV>::BM;
+    constexpr int NWAVES = BM / 32;
+    constexpr int CBLK = DV / 32;
+    constexpr int OWAVE = CBLK * 16 * 64;
+    const int item = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int mblk = item % p.n_mblocks;
+    const int bh = item / p.n_mblocks;
+    const int h = bh % p.hq;
+    const int bb = bh / p.hq;
+    const int my_row = mblk * BM + wave * 32 + col;
+    const int64_t slot0 = static_cast<int64_t>(item) * p.n_split * NWAVES + wave;
+    const f32x2* pml = reinterpret_cast<const f32x2*>(p.split_ml) + slot0 * 64 + lane;
+    float mmax = kNegInf;
+    for (int i = 0; i < p.n_split; ++i) mmax = fmaxf(mmax, pml[i * NWAVES * 64][0]);
+    f32x16 acc[CBLK];
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16{};
+    float lsum = 0.f;
+    for (int i = 0; i < p.n_split; ++i) {
+        const f32x2 ml = pml[i * NWAVES * 64];
+        const float w = ml[0] == kNegInf ? 0.f : fast_exp2(ml[0] - mmax);
+        lsum = fmaf(w, ml[1], lsum);
+        const float* po = p.split_o + (slot0 + static_cast<int64_t>(i) * NWAVES) * OWAVE;
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(po + ((cb * 4 + q4) * 64 + lane) * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[cb][4 * q4 + r] = fmaf(w, x[r], acc[cb][4 * q4 + r]);
+            }
+        }
+    }
+    if (my_row < p.sq) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t* orow = static_cast<uint16_t*>(p.o) +
+                         (static_cast<int64_t>(bb) * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss);
+        store_o_row<CBLK>(orow, acc, inv, half);
+        if (p.lse != nullptr && half == 0) {
+            const float lse = lsum > 0.f ? (mmax + __log2f(lsum)) * kLn2 : kNegInf;
+            p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
+        }
+    }
+}
+
 template <int DQK, int DV, bool CAUSAL, bool VARLEN>
 hipError_t launch(AttnParams p, hipStream_t stream) {
     constexpr int BM = TileCfg<DQK, DV>::BM;
@@ -699,16 +793,32 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     // sequences pair only on grids of at most 8 rounds: their workgroups are dealt to the XCDs
     // by (sequence, kv head), and pairing the 32-sequence workload's 8192-row grid cost +11%.
     const bool ext = p.window_left >= 0 || (!CAUSAL && p.window_right >= 0) || p.sinks != nullptr;
+    if (p.n_split > 1) {
+        if constexpr (CAUSAL || VARLEN) {
+            return hipErrorInvalidValue;
+        } else {
+            if (ext || p.split_ml == nullptr || p.split_o == nullptr) return hipErrorInvalidValue;
+            const int64_t nwg = blocks * p.n_split;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>),
+                               dim3(static_cast<unsigned>(nwg)), dim3(BM * 2), 0, stream, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((attn_split_merge<DQK, DV>), dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
     if (ext) {
         if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, true>),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, true, false>),
                            dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0, stream, p);
         return hipGetLastError();
     }
     bool paired = CAUSAL && p.n_mblocks > 1;
     if (paired && VARLEN) {
         int groups = 0;
-        const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false>;
+        const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false, false>;
         const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2, &groups);
         if (e != hipSuccess) return e;
         paired = blocks <= 8 * static_cast<int64_t>(groups);
@@ -716,10 +826,10 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     const int64_t nwg = paired ? static_cast<int64_t>(p.b) * p.hq * ((p.n_mblocks + 1) / 2) : blocks;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
     if (paired) {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false>), dim3(static_cast<unsigned>(nwg)),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false, false>), dim3(static_cast<unsigned>(nwg)),
                            dim3(BM * 2), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, false>), dim3(static_cast<unsigned>(nwg)),
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, false, false>), dim3(static_cast<unsigned>(nwg)),
                            dim3(BM * 2), 0, stream, p);
     }
     return hipGetLastError();
@@ -743,6 +853,66 @@ hipError_t launch_dims(const AttnParams& p, int d_qk, int d_v, bool causal, hipS
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool causal, hipStream_t stream) {
     return p.cu_q != nullptr ? launch_dims<true>(p, d_qk, d_v, causal, stream)
                              : launch_dims<false>(p, d_qk, d_v, causal, stream);
+}
+
+namespace {
+
+// rows per workgroup and the split kernel of a head-dim pair (nullptr: not built)
+template <int DQK, int DV>
+const void* split_kernel(int* bm) {
+    *bm = TileCfg<DQK, DV>::BM;
+    return reinterpret_cast<const void*>(attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>);
+}
+
+const void* split_kernel_for(int d_qk, int d_v, int* bm) {
+    if (d_qk == 32 && d_v == 32) return split_kernel<32, 32>(bm);
+    if (d_qk == 64 && d_v == 64) return split_kernel<64, 64>(bm);
+    if (d_qk == 128 && d_v == 128) return split_kernel<128, 128>(bm);
+    if (d_qk == 192 && d_v == 128) return split_kernel<192, 128>(bm);
+    return nullptr;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t attn_bf16_split_layout(int b, int hq, int sq, int d_qk, int d_v, int n_split, size_t offsets[2]) {
+    int bm = 0;
+    if (split_kernel_for(d_qk, d_v, &bm) == nullptr || b < 0 || hq < 0 || sq < 0 || n_split < 1) return 0;
+    const size_t blocks = static_cast<size_t>(b) * hq * ((static_cast<size_t>(sq) + bm - 1) / bm);
+    const size_t waves = static_cast<size_t>(bm / 32);
+    offsets[0] = 0;
+    offsets[1] = round256(blocks * n_split * waves * 64 * 2 * sizeof(float));
+    return offsets[1] + round256(blocks * n_split * static_cast<size_t>(bm) * d_v * sizeof(float));
+}
+
+hipError_t attn_bf16_split_plan(int b, int hq, int sq, int sk, int d_qk, int d_v, bool causal, int* n_split) {
+    *n_split = 1;
+    int bm = 0;
+    const void* kernel = split_kernel_for(d_qk, d_v, &bm);
+    if (kernel == nullptr || causal || b <= 0 || hq <= 0 || sq <= 0 || sk <= 0) return hipSuccess;
+    int slots = 0;
+    const hipError_t e = resident_groups(kernel, bm * 2, &slots);
+    if (e != hipSuccess) return e;
+    // Time in units of one key tile of one workgroup: rounds of resident workgroups times the
+    // tiles each runs, plus about two tiles per split workgroup for writing its partial and the
+    // merge.  A split must be predicted 10% faster, and each range must hold enough work that
+    // the merge kernel's launch and traffic stay small beside it: keys x (d_qk + d_v) >= 2^18,
+    // 1024 keys at d128 (measured on MI355X: the d128 8192^2 GQA 5:1 shape gains 12% at three
+    // ranges; a d32 2048^2 shape of 256 blocks loses at every split).
+    const int64_t blocks = static_cast<int64_t>(b) * hq * ((sq + bm - 1) / bm);
+    const int nt = (sk + 63) / 64;
+    auto rounds = [&](int64_t wgs) { return static_cast<double>((wgs + slots - 1) / slots); };
+    double best = rounds(blocks) * nt;
+    for (int s = 2; s <= 8 && static_cast<int64_t>(nt / s) * 64 * (d_qk + d_v) >= (int64_t(1) << 18); ++s) {
+        if (blocks * s > INT32_MAX) break;
+        const double cost = rounds(blocks * s) * (static_cast<double>(nt) / s + 2.0);
+        if (cost < 0.9 * best) {
+            best = cost;
+            *n_split = s;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace mha

@@ -111,6 +111,8 @@ mha_status check_common(int b, int hq, int hk, int sq, int sk, float scale, int 
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+constexpr int kMaxSplit = 16;   // key ranges per query block of the split call
+
 }  // namespace
 
 extern "C" {
@@ -141,7 +143,7 @@ namespace {
 mha_status fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride, const void* v,
                     mha_strides v_stride, void* o, mha_strides o_stride, float* lse, int b, int hq, int hk, int sq,
                     int sk, int d_qk, int d_v, float softmax_scale, int causal, int window_left, int window_right,
-                    const float* sinks, void* stream) {
+                    const float* sinks, int n_split, void* ws, size_t ws_bytes, void* stream) {
     mha_status st = check_common(b, hq, hk, sq, sk, softmax_scale, causal);
     if (st != MHA_OK) return st;
     if (window_left < -1 || window_right < -1)
@@ -193,6 +195,23 @@ mha_status fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_stri
     p.window_left = window_left >= sq ? -1 : window_left;
     p.window_right = (causal || window_right >= sk) ? -1 : window_right;
     p.sinks = sinks;
+    if (n_split < 1 || n_split > kMaxSplit)
+        return fail(MHA_ERR_VALUE, "n_split = %d: must be in [1, %d]", n_split, kMaxSplit);
+    if (n_split > 1) {
+        if (causal) return fail(MHA_ERR_UNSUPPORTED, "the key-range split runs on non-causal attention only");
+        const int nt = (sk + 63) / 64;
+        if (n_split > nt)
+            return fail(MHA_ERR_VALUE, "n_split = %d exceeds the %d key tiles of 64 (sk = %d)", n_split, nt, sk);
+        size_t off[2];
+        const size_t need = mha::attn_bf16_split_layout(b, hq, sq, d_qk, d_v, n_split, off);
+        if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);
+        if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MHA_ERR_WORKSPACE, "ws must be 256-byte aligned");
+        if (ws_bytes < need) return fail(MHA_ERR_WORKSPACE, "ws_bytes = %zu < required %zu", ws_bytes, need);
+        char* w = static_cast<char*>(ws);
+        p.n_split = n_split;
+        p.split_ml = reinterpret_cast<float*>(w + off[0]);
+        p.split_o = reinterpret_cast<float*>(w + off[1]);
+    }
     return launched(mha::launch_attn_fwd_bf16(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)),
                     "attn_fwd_bf16", stream);
 }
@@ -206,7 +225,38 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_
                         int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
                         int causal, void* stream) {
     return fwd_bf16(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, b, hq, hk, sq, sk, d_qk, d_v,
-                    softmax_scale, causal, -1, -1, nullptr, stream);
+                    softmax_scale, causal, -1, -1, nullptr, 1, nullptr, 0, stream);
+}
+
+mha_status mha_fwd_bf16_split_plan(int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, int causal,
+                                   int* n_split) {
+    if (!n_split) return fail(MHA_ERR_NULL, "n_split is NULL");
+    *n_split = 1;
+    mha_status st = check_common(b, hq, hk, sq, sk, 1.f, causal);
+    if (st != MHA_OK) return st;
+    if (!supported_bf16(d_qk, d_v))
+        return fail(MHA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (32,32) (64,64) (128,128) (192,128)",
+                    d_qk, d_v);
+    const hipError_t e = mha::attn_bf16_split_plan(b, hq, sq, sk, d_qk, d_v, causal != 0, n_split);
+    if (e != hipSuccess) {
+        *n_split = 1;
+        return fail(MHA_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+size_t mha_fwd_bf16_split_workspace_bytes(int b, int hq, int sq, int d_qk, int d_v, int n_split) {
+    if (n_split <= 1 || n_split > kMaxSplit) return 0;
+    size_t off[2];
+    return mha::attn_bf16_split_layout(b, hq, sq, d_qk, d_v, n_split, off);
+}
+
+mha_status mha_fwd_bf16_split(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
+                              const void* v, mha_strides v_stride, void* o, mha_strides o_stride, float* lse,
+                              int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, float softmax_scale,
+                              int causal, int n_split, void* ws, size_t ws_bytes, void* stream) {
+    return fwd_bf16(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, b, hq, hk, sq, sk, d_qk, d_v,
+                    softmax_scale, causal, -1, -1, nullptr, n_split, ws, ws_bytes, stream);
 }
 
 mha_status mha_fwd_bf16_window_sink(const void* q, mha_strides q_stride, const void* k, mha_strides k_stride,
@@ -215,7 +265,7 @@ mha_status mha_fwd_bf16_window_sink(const void* q, mha_strides q_stride, const v
                                     int causal, int window_left, int window_right, const float* sinks,
                                     void* stream) {
     return fwd_bf16(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, b, hq, hk, sq, sk, d_qk, d_v,
-                    softmax_scale, causal, window_left, window_right, sinks, stream);
+                    softmax_scale, causal, window_left, window_right, sinks, 1, nullptr, 0, stream);
 }
 
 }  // extern "C"

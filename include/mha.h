@@ -103,6 +103,60 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride,
                         float softmax_scale, int causal, void* stream);
 
 /*
+ * mha_fwd_bf16_split - mha_fwd_bf16 with each query block's keys divided among
+ * n_split workgroups, for grids of few query blocks that would leave compute
+ * units idle: the per-rank shapes of "Tune MHA config & small-head pipeline
+ * pathology" (The 8 remaining regressions: d128 8192^2 at TP8, hq8/hk1 and
+ * hq5/hk1), whose 320-512 query blocks of 128 rows are one round of the
+ * device or less.  Each workgroup runs keys [t0*64, t1*64) for its range of
+ * the ceil(sk/64) key tiles (the ranges differ by at most one tile) and leaves
+ * its fp32 state in the workspace; a second kernel on the same stream merges
+ * the ranges in ascending order through the softmax identity over a union of
+ * key sets,
+ *   O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i,
+ * which is the LSE merge of the same page's outputs (O, LSE).  The result is
+ * deterministic but not bitwise the unsplit one: the probabilities are rounded
+ * to bf16 against each range's own reference max and the sums run in another
+ * order (both within the unsplit call's error bounds).
+ *
+ *   n_split  1 (exactly mha_fwd_bf16; ws ignored) to 16; above 1 only with
+ *            causal = 0 (else MHA_ERR_UNSUPPORTED) and at most ceil(sk/64)
+ *            (else MHA_ERR_VALUE)
+ *   ws       device workspace of at least
+ *            mha_fwd_bf16_split_workspace_bytes(b, hq, sq, d_qk, d_v, n_split)
+ *            bytes, 256-byte aligned (else MHA_ERR_WORKSPACE).  Its contents
+ *            need no initialisation and are scratch after the call; calls that
+ *            overlap in time (another stream) need separate workspaces.
+ * Everything else (shapes, layouts, errors) as mha_fwd_bf16.  Two kernels run
+ * on `stream`: the attention kernel over b*hq*blocks*n_split workgroups, then
+ * the merge over b*hq*blocks.
+ */
+mha_status mha_fwd_bf16_split(const void* q, mha_strides q_stride,
+                              const void* k, mha_strides k_stride,
+                              const void* v, mha_strides v_stride,
+                              void* o, mha_strides o_stride,
+                              float* lse,
+                              int b, int hq, int hk, int sq, int sk, int d_qk, int d_v,
+                              float softmax_scale, int causal,
+                              int n_split, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace mha_fwd_bf16_split needs for n_split ranges: per query
+ * block (128 rows; 256 for d_qk = 192), range and row an fp32 (max, sum) pair
+ * for each of the row's two lanes and d_v fp32 partial outputs.  0 for
+ * n_split <= 1, n_split above 16 or an unsupported head-dim pair. */
+size_t mha_fwd_bf16_split_workspace_bytes(int b, int hq, int sq, int d_qk, int d_v, int n_split);
+
+/* The n_split that balances this shape's grid on the CURRENT device (its
+ * compute units times the workgroups each holds): 1 when the unsplit grid
+ * already fills it, for causal attention and for empty shapes; otherwise the
+ * split (2..8) that a model of whole rounds of resident workgroups predicts at
+ * least 10% faster, among those whose ranges keep keys * (d_qk + d_v) >= 2^18
+ * (the merge kernel's cost stays small beside each range's work).  Shape errors as
+ * mha_fwd_bf16; MHA_ERR_HIP if the device cannot be queried (then *n_split = 1). */
+mha_status mha_fwd_bf16_split_plan(int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, int causal,
+                                   int* n_split);
+
+/*
  * mha_fwd_bf16_window_sink - mha_fwd_bf16 with a sliding window and per-head
  * attention sinks: the GPT-OSS "sink+sliding-window" shapes named in the Test
  * Result section of "Tune MHA config & small-head pipeline pathology".

@@ -85,6 +85,56 @@ def test_bf16_empty_problem_is_a_noop(lib):
     assert _bf16(lib, b=0)[0] == 0
 
 
+def _split(lib, **kw):
+    a = dict(q=FAKE, qs=_bshd(1000, 2, 128), k=FAKE, ks=_bshd(1000, 2, 128), v=FAKE, vs=_bshd(1000, 2, 128),
+             o=FAKE, os=_bshd(1000, 2, 128), lse=None, b=1, hq=2, hk=2, sq=1000, sk=1000, dqk=128, dv=128,
+             scale=0.088, causal=0, n=3, ws=FAKE, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.mha_fwd_bf16_split_workspace_bytes(a["b"], a["hq"], a["sq"], a["dqk"], a["dv"], max(a["n"], 2))
+    st = lib.mha_fwd_bf16_split(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"], a["lse"],
+                                a["b"], a["hq"], a["hk"], a["sq"], a["sk"], a["dqk"], a["dv"], a["scale"],
+                                a["causal"], a["n"], a["ws"], a["wsb"], None)
+    return st, lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(causal=1), 3, "non-causal attention only"),
+    (dict(n=0), 8, "n_split = 0"),
+    (dict(n=17), 8, "n_split = 17"),
+    (dict(n=4, sk=150, ks=_bshd(150, 2, 128), vs=_bshd(150, 2, 128)), 8, "exceeds the 3 key tiles"),
+    (dict(ws=None), 6, "ws is NULL"),
+    (dict(ws=FAKE + 16), 6, "256-byte aligned"),
+    (dict(wsb=4096), 6, "ws_bytes = 4096"),
+    (dict(hq=3), 2, "multiple of hk"),
+    (dict(q=FAKE + 2), 4, "q: pointer must be 16-byte aligned"),
+])
+def test_split_refusals(lib, kw, status, needle):
+    st, msg = _split(lib, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_split_workspace_bytes(lib):
+    # per 128-row query block, range, wave and lane an fp32 (max, sum) pair; per block, range and
+    # row d_v fp32 partial outputs; regions 256-byte aligned
+    ws = lib.mha_fwd_bf16_split_workspace_bytes
+    blocks = 2 * 5 * 8    # b 2, hq 5, 1000 rows
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert ws(2, 5, 1000, 128, 128, 3) == r256(blocks * 3 * 4 * 64 * 8) + blocks * 3 * 128 * 128 * 4
+    # d_qk 192: 256-row blocks of 8 waves
+    assert ws(1, 2, 1000, 192, 128, 2) == r256(8 * 2 * 8 * 64 * 8) + 8 * 2 * 256 * 128 * 4
+    assert ws(1, 2, 1000, 128, 128, 1) == 0 and ws(1, 2, 1000, 128, 128, 17) == 0
+    assert ws(1, 2, 1000, 96, 96, 2) == 0
+
+
+def test_split_plan_refusals(lib):
+    n = ctypes.c_int(7)
+    assert lib.mha_fwd_bf16_split_plan(1, 3, 2, 100, 100, 128, 128, 0, ctypes.byref(n)) == 2 and n.value == 1
+    assert lib.mha_fwd_bf16_split_plan(1, 2, 2, 100, 100, 96, 96, 0, ctypes.byref(n)) == 3
+    assert lib.mha_fwd_bf16_split_plan(1, 2, 2, 100, 100, 128, 128, 0, None) == 1
+
+
 def _varlen(lib, **kw):
     a = dict(q=FAKE, qs=S(0, 2 * 64, 64), k=FAKE, ks=S(0, 2 * 64, 64), v=FAKE, vs=S(0, 2 * 64, 64),
              o=FAKE, os=S(0, 2 * 64, 64), lse=None, cuq=FAKE, cuk=FAKE, b=3, hq=2, hk=2, tq=300, tk=300,

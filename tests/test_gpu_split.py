@@ -1,0 +1,134 @@
+"""GPU parity of the key-range split (mha_fwd_bf16_split) against the float64 oracle.
+
+Each query block's keys are divided among n_split workgroups whose partial states a second
+kernel merges; the oracle knows nothing of the split, so these tests check that the ranges
+cover every key once, that the merge weights are right (including ranges whose maxima lie far
+apart) and that nothing depends on what the workspace held before the call.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import assert_bf16_parity, oracle_heads, require_gpu, scale_for, to_np
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_SHAPES = [
+    # b, hq, hk, sq, sk, d_qk, d_v, n_split
+    (1, 2, 1, 200, 1000, 32, 32, 3),       # 16 key tiles -> 5/5/6, ragged tail (1000 = 15*64 + 40)
+    (2, 3, 1, 130, 777, 64, 64, 5),        # 13 tiles -> 2/3/2/3/3, two query blocks (ragged)
+    (1, 4, 2, 257, 1100, 128, 128, 2),     # GQA 2:1, three query blocks
+    (1, 5, 1, 128, 640, 128, 128, 10),     # GQA 5:1, one tile per range
+    (1, 2, 2, 300, 700, 192, 128, 4),      # 256-row blocks of 8 waves
+    (1, 2, 1, 64, 4096, 128, 128, 16),     # the largest split, 4 tiles per range
+]
+
+
+def _lib():
+    import head_attention_forward_flash_amd as mha
+    return mha
+
+
+def _inputs(shape, seed):
+    b, hq, hk, sq, sk, dqk, dv, _ = shape
+    q = workloads.make_random((b, sq, hq, dqk), seed)
+    k = workloads.make_random((b, sk, hk, dqk), seed + 1)
+    v = workloads.make_random((b, sk, hk, dv), seed + 2)
+    return q, k, v
+
+
+def _run(q, k, v, n_split, workspace=None, scale=None):
+    dev = require_gpu()
+    o, lse = _lib().mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=False, softmax_scale=scale,
+                                 n_split=n_split, workspace=workspace)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check(q, k, v, o, lse, scale, what):
+    b, hq = q.shape[0], q.shape[2]
+    for bb in range(b):
+        o_ref, l_ref = oracle_heads(q, k, v, list(range(hq)), None, scale=scale, causal=False, batch=bb)
+        assert_bf16_parity(to_np(o[bb]), o_ref, lse[bb].numpy().astype(np.float64), l_ref, f"{what} b={bb}")
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"b{s[0]}h{s[1]}/{s[2]}q{s[3]}k{s[4]}d{s[5]}-{s[6]}x{s[7]}"
+                                                      for s in SPLIT_SHAPES])
+def test_split_matches_oracle(shape):
+    q, k, v = _inputs(shape, 2000 + sum(shape))
+    o, lse = _run(q, k, v, shape[-1])
+    _check(q, k, v, o, lse, scale_for(shape[5]), f"split {shape}")
+
+
+def test_split_is_deterministic_and_ignores_workspace_contents():
+    # every workspace word the merge reads is written by the same call, whatever the workspace
+    # held; the merge adds the ranges in one fixed order
+    dev = require_gpu()
+    shape = (1, 5, 1, 640, 2048, 128, 128, 6)
+    q, k, v = _inputs(shape, 77)
+    b, hq, hk, sq, sk, dqk, dv, n = shape
+    need = _lib().mha_fwd_bf16_split_workspace_bytes(b, hq, sq, dqk, dv, n)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    first = _run(q, k, v, n, workspace=ws)
+    for fill in (0x00, 0x7F):
+        ws.fill_(fill)
+        again = _run(q, k, v, n, workspace=ws)
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1]), fill
+    _check(q, k, v, first[0], first[1], scale_for(dqk), "deterministic split")
+
+
+def test_split_workspace_reused_by_a_smaller_call():
+    # one workspace, two calls in a row on the stream: the second (fewer blocks, another split)
+    # finds the first call's partials and must not be confused by them
+    dev = require_gpu()
+    big = (2, 4, 2, 384, 1500, 64, 64, 7)
+    small = (1, 2, 2, 130, 900, 64, 64, 3)
+    need = _lib().mha_fwd_bf16_split_workspace_bytes(2, 4, 384, 64, 64, 7)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    for shape, seed in ((big, 91), (small, 92)):
+        q, k, v = _inputs(shape, seed)
+        o, lse = _run(q, k, v, shape[-1], workspace=ws)
+        _check(q, k, v, o, lse, scale_for(shape[5]), f"reused workspace {shape}")
+
+
+@pytest.mark.parametrize("dims", [(32, 32), (64, 64), (128, 128), (192, 128)])
+def test_split_ranges_far_apart(dims):
+    # Query channel 0 is 1 and one key scores ~150 above the rest, in the middle range of three:
+    # the other ranges' weights 2^(m_i - M) underflow to 0 in the merge.  A key ~150 below the
+    # rest sits in the first range, whose max stays that of the ordinary keys.
+    dqk, dv = dims
+    sq, sk, n = 160, 960, 3
+    q = workloads.make_random((1, sq, 2, dqk), 61 + dqk).float()
+    k = workloads.make_random((1, sk, 1, dqk), 62 + dqk).float()
+    v = workloads.make_random((1, sk, 1, dv), 63 + dqk)
+    q[..., 0] = 1.0
+    k[0, 480, :, 0] = 150.0 * dqk ** 0.5
+    k[0, 100, :, 0] = -150.0 * dqk ** 0.5
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o, lse = _run(q, k, v, n)
+    _check(q, k, v, o, lse, scale_for(dqk), f"spiked split d{dqk}")
+
+
+def test_split_against_unsplit_and_plan():
+    dev = require_gpu()
+    mha = _lib()
+    # the TP8 rank shapes: 320 query blocks of GQA 5:1 leave most compute units with one
+    # workgroup, so the plan splits them; 512 blocks of GQA 8:1 fill the device, so it does not
+    n5 = mha.mha_fwd_bf16_split_plan(1, 5, 1, 8192, 8192, 128, 128, False)
+    n8 = mha.mha_fwd_bf16_split_plan(1, 8, 1, 8192, 8192, 128, 128, False)
+    assert n5 > 1 and n8 == 1, (n5, n8)
+    assert mha.mha_fwd_bf16_split_plan(1, 5, 1, 8192, 8192, 128, 128, True) == 1
+    assert mha.mha_fwd_bf16_split_plan(1, 2, 2, 128, 128, 64, 64, False) == 1   # two key tiles
+    # The same inputs through both kernels.  They differ in which reference max each probability
+    # is rounded to bf16 against (the row sum adds the rounded values), so ln l moves by the
+    # random bf16 rounding of thousands of terms: the oracle's LSE bound, 2^-8, holds for both.
+    shape = (1, 5, 1, 512, 3000, 128, 128, n5)
+    q, k, v = _inputs(shape, 88)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o1, l1 = mha.mha_fwd_bf16(qd, kd, vd, n_split=1)
+    o2, l2 = mha.mha_fwd_bf16(qd, kd, vd, n_split=n5)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2.0 ** -7
+    assert (l1 - l2).abs().max().item() <= 2.0 ** -8

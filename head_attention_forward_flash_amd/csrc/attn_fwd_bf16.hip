@@ -724,18 +724,21 @@ item_done: __attribute__((unused));
     }
 }
 
-// The key-range split's second kernel: one workgroup per query block, laid out like the
-// attention kernel's (one wave per 32 rows, the same lanes), merges the n_split partial states in
-// ascending order of key range.  The softmax over the union of the ranges is
+// The key-range split's second kernel: one workgroup per (query block, 32-channel block of O),
+// laid out like the attention kernel (one wave per 32 rows, the same lanes), merges the n_split
+// partial states in ascending order of key range.  The softmax over the union of the ranges is
 //   O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,   M = max_i m_i   (base-2 units),
-// and LSE = (M + log2 of the denominator) ln 2, so the result does not depend on timing.
+// and LSE = (M + log2 of the denominator) ln 2, so the result does not depend on timing.  (Every
+// channel block's workgroup recomputes the row's weights from the same values, in the same
+// order; the first one writes the LSE.)
 template <int DQK, int DV>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2)) void attn_split_merge(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;
     constexpr int NWAVES = BM / 32;
     constexpr int CBLK = DV / 32;
     constexpr int OWAVE = CBLK * 16 * 64;
-    const int item = blockIdx.x;
+    const int cb = blockIdx.x % CBLK;
+    const int item = blockIdx.x / CBLK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -750,9 +753,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2)) void attn_split_merge(c
     const f32x2* pml = reinterpret_cast<const f32x2*>(p.split_ml) + slot0 * 64 + lane;
     float mmax = kNegInf;
     for (int i = 0; i < p.n_split; ++i) mmax = fmaxf(mmax, pml[i * NWAVES * 64][0]);
-    f32x16 acc[CBLK];
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16{};
+    f32x16 acc[1] = {f32x16{}};
     float lsum = 0.f;
     for (int i = 0; i < p.n_split; ++i) {
         const f32x2 ml = pml[i * NWAVES * 64];
@@ -760,21 +761,18 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2)) void attn_split_merge(c
         lsum = fmaf(w, ml[1], lsum);
         const float* po = p.split_o + (slot0 + static_cast<int64_t>(i) * NWAVES) * OWAVE;
 #pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(po + ((cb * 4 + q4) * 64 + lane) * 4);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(po + ((cb * 4 + q4) * 64 + lane) * 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[cb][4 * q4 + r] = fmaf(w, x[r], acc[cb][4 * q4 + r]);
-            }
+            for (int r = 0; r < 4; ++r) acc[0][4 * q4 + r] = fmaf(w, x[r], acc[0][4 * q4 + r]);
         }
     }
     if (my_row < p.sq) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         uint16_t* orow = static_cast<uint16_t*>(p.o) +
-                         (static_cast<int64_t>(bb) * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss);
-        store_o_row<CBLK>(orow, acc, inv, half);
-        if (p.lse != nullptr && half == 0) {
+                         (static_cast<int64_t>(bb) * p.ov.sb + h * p.ov.sh + my_row * p.ov.ss) + cb * 32;
+        store_o_row<1>(orow, acc, inv, half);
+        if (cb == 0 && p.lse != nullptr && half == 0) {
             const float lse = lsum > 0.f ? (mmax + __log2f(lsum)) * kLn2 : kNegInf;
             p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
         }
@@ -799,13 +797,13 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
         } else {
             if (ext || p.split_ml == nullptr || p.split_o == nullptr) return hipErrorInvalidValue;
             const int64_t nwg = blocks * p.n_split;
-            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            if (nwg > INT32_MAX || blocks * (DV / 32) > INT32_MAX) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>),
                                dim3(static_cast<unsigned>(nwg)), dim3(BM * 2), 0, stream, p);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((attn_split_merge<DQK, DV>), dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0,
-                               stream, p);
+            hipLaunchKernelGGL((attn_split_merge<DQK, DV>), dim3(static_cast<unsigned>(blocks * (DV / 32))), dim3(BM * 2),
+                               0, stream, p);
             return hipGetLastError();
         }
     }

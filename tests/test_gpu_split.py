@@ -132,3 +132,23 @@ def test_split_against_unsplit_and_plan():
     torch.cuda.synchronize()
     assert (o1.float() - o2.float()).abs().max().item() <= 2.0 ** -7
     assert (l1 - l2).abs().max().item() <= 2.0 ** -8
+
+
+def test_split_on_strided_views():
+    # q, k, v as head slices of wider tensors and o written into a slice of a wider buffer: the
+    # split kernel takes the same strides as the unsplit one
+    dev = require_gpu()
+    mha = _lib()
+    base_q = workloads.make_random((2, 300, 6, 64), 71)
+    base_k = workloads.make_random((2, 900, 4, 64), 72)
+    base_v = workloads.make_random((2, 900, 4, 64), 73)
+    q, k, v = base_q[:, :, 1:4], base_k[:, :, 2:3], base_v[:, :, 0:1]
+    out_buf = torch.zeros((2, 300, 8, 64), dtype=torch.bfloat16, device=dev)
+    out = out_buf[:, :, 2:5]
+    o, lse = mha.mha_fwd_bf16(base_q.to(dev)[:, :, 1:4], base_k.to(dev)[:, :, 2:3], base_v.to(dev)[:, :, 0:1],
+                              out=out, n_split=4)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    ob = out_buf.cpu()
+    assert torch.all(ob[:, :, :2] == 0) and torch.all(ob[:, :, 5:] == 0)
+    _check(q, k, v, ob[:, :, 2:5], lse.cpu(), scale_for(64), "strided split")

@@ -51,7 +51,8 @@ PAGES_FP8_CALL_US = {"fp8_ksmooth_d128": 219.2, "fp8_long_h5": 3857.2, "mxfp8_ks
 # The five configs the metric is quoted on, in order, and the further shapes timed beside them.
 CONFIGS = [("c1", "tiny_d64"), ("c2", "gqa_d64_causal"), ("c3", "gqa_d128_causal"),
            ("c4", "mla_d192_d128_causal"), ("c5", "fp8_ksmooth_d128")]
-EXTRA = ["gqa8_d128_tp8_noncausal", "gqa5_d128_tp8_noncausal", "mla_d192_d128_noncausal",
+EXTRA = ["gqa8_d128_tp8_noncausal", "gqa5_d128_tp8_noncausal", "gqa8_d128_tp8_causal", "gqa5_d128_tp8_causal",
+         "mla_d192_d128_noncausal",
          "gqa_d128_8192_causal", "mla_d192_d128_tp8_causal", "gptoss_swa_sink_d64", "gptoss_sink_d64",
          "vd32_noncausal", "mxfp8_ksmooth_d128", "fp8_long_h5", "varlen:varlen_gqa_d128_causal"]
 

@@ -48,6 +48,8 @@
 // Every global load goes through a buffer resource clamped to the (batch, head)
 // slice, so rows past sq / sk read as zero instead of faulting.
 
+#include <algorithm>
+#include <cstdint>
 #include <type_traits>
 #include <utility>
 
@@ -108,10 +110,17 @@ template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, EAR
 template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, EARLY = MHA_EARLY_WIDE; };
 template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, EARLY = MHA_EARLY_WIDE; };
 
+// Key tiles of causal query block m (keys [0, min(sk, (m + 1) BM))).
+template <int BM, int BN>
+__host__ __device__ __forceinline__ int split_causal_tiles(int m, int sk) {
+    const int64_t keys = static_cast<int64_t>(m + 1) * BM < sk ? static_cast<int64_t>(m + 1) * BM : sk;
+    return static_cast<int>((keys + BN - 1) / BN);
+}
+
 // EXT: sliding window (keys j with i - window_left <= j <= i + window_right, positions inside
-// the sequence) and per-head sink logits.  SPLIT: p.n_split workgroups per query block, each over
-// one contiguous range of key tiles (dense, non-causal grids that would underfill the device),
-// leaving partial states for attn_split_merge.
+// the sequence) and per-head sink logits.  SPLIT: grids that would underfill the device give each
+// query block (non-causal) or each pair of causal blocks (n-1-j, j) p.n_split workgroups, each
+// over one contiguous range of the key tiles, which leave partial states for attn_split_merge.
 template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_kernel(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
@@ -151,7 +160,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
     //      the same work and the grid has no tail of light workgroups.
     static_assert(CAUSAL || !PAIRED, "only causal blocks differ in work");
     static_assert(!EXT || !PAIRED, "windows and sinks run on unpaired grids");
-    static_assert(!SPLIT || (!CAUSAL && !VARLEN && !EXT), "the key split runs on dense, non-causal grids");
+    static_assert(!SPLIT || (!VARLEN && !EXT && CAUSAL == PAIRED), "the key split runs on dense grids, paired when causal");
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
@@ -171,13 +180,35 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), 2) void attn_fwd_bf16_k
             lid = pid;
         }
     }
-    // SPLIT: the key ranges of one query block are consecutive ids (one XCD), range fastest
+    // SPLIT: the key ranges of one query block (or pair) are consecutive ids (one XCD), range fastest
     const int split = SPLIT ? lid % p.n_split : 0;
     if constexpr (SPLIT) lid /= p.n_split;
-    [[maybe_unused]] const int item = lid;    // (batch, head, query block) of this workgroup
+    [[maybe_unused]] const int item = lid;    // (batch, head, query block or pair) of this workgroup
     const int mrev = lid % per_head;
     const int bh = lid / per_head;
     int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: heavy blocks first
+    // SPLIT && CAUSAL: the pair's key tiles, block n-1-j's then block j's, in one sequence of
+    // L = LA + LB tiles; this workgroup takes tiles [a, b) of it, as the tail [a, min(b, LA)) of
+    // the first block and, if b > LA, the head [0, b - LA) of the second.  `which` is the block
+    // in hand (0: n-1-j, 1: j) and [seg0, seg1) its tiles.
+    [[maybe_unused]] int which = 0, seg0 = 0, seg1 = 0, pair_la = 0, pair_lb = 0, pair_b = 0;
+    if constexpr (SPLIT && CAUSAL) {
+        const int ma = p.n_mblocks - 1 - mrev;
+        pair_la = split_causal_tiles<BM, BN>(ma, p.sk);
+        pair_lb = ma != mrev ? split_causal_tiles<BM, BN>(mrev, p.sk) : 0;
+        const int len = pair_la + pair_lb;
+        const int a = split * len / p.n_split;
+        pair_b = (split + 1) * len / p.n_split;
+        if (a < pair_la) {
+            seg0 = a;
+            seg1 = min(pair_b, pair_la);
+        } else {
+            mblk = mrev;
+            which = 1;
+            seg0 = a - pair_la;
+            seg1 = pair_b - pair_la;
+        }
+    }
     bool lds_zeroed = false;
 next_item:
     // A pair's second block passes the lane index through an empty asm statement: nothing
@@ -253,12 +284,18 @@ next_item:
             if (p.window_left >= 0) t0 = max(0, mblk * BM - p.window_left) / BN;
         }
         if constexpr (SPLIT) {
-            // key tiles [t0, t1) of the ceil(sk / BN); the ranges differ by at most one tile.  The
-            // K and V slices end at the range, so the DMA that runs ahead of the last tile reads
-            // nothing past it.
-            const int nt = (sk + BN - 1) / BN;
-            t0 = split * nt / p.n_split;
-            kv_end = min(sk, (split + 1) * nt / p.n_split * BN);
+            // key tiles [t0, t1): non-causal, range `split` of the ceil(sk / BN) tiles (the ranges
+            // differ by at most one tile); causal, the segment of the block in hand.  The K and V
+            // slices end at the range, so the DMA that runs ahead of the last tile reads nothing
+            // past it.
+            if constexpr (CAUSAL) {
+                t0 = seg0;
+                kv_end = min(kv_end, seg1 * BN);
+            } else {
+                const int nt = (sk + BN - 1) / BN;
+                t0 = split * nt / p.n_split;
+                kv_end = min(sk, (split + 1) * nt / p.n_split * BN);
+            }
             if (kv_end < sk) {
                 kslice = static_cast<uint32_t>((static_cast<int64_t>(kv_end - 1) * p.kv.ss + DQK) * 2);
                 vslice = static_cast<uint32_t>((static_cast<int64_t>(kv_end - 1) * p.vv.ss + DV) * 2);
@@ -677,7 +714,7 @@ next_item:
             // this key range's state goes to the workspace and the merge kernel finishes the row:
             // O unnormalised, in accumulator order (the merge reads it back lane for lane), and
             // per lane the base-2 reference max and the row sum
-            const int64_t slot = (static_cast<int64_t>(item) * p.n_split + split) * NWAVES + wave;
+            const int64_t slot = ((static_cast<int64_t>(item) * p.n_split + split) * (CAUSAL ? 2 : 1) + which) * NWAVES + wave;
             float* po = p.split_o + slot * (CBLK * 16 * 64);
 #pragma unroll
             for (int cb = 0; cb < CBLK; ++cb) {
@@ -688,7 +725,8 @@ next_item:
                 }
             }
             reinterpret_cast<f32x2*>(p.split_ml)[slot * 64 + lane] = f32x2{m_log2, l_tot};
-            return;
+            if constexpr (PAIRED) goto item_done;
+            else return;
         }
         if constexpr (EXT) {
             // the head's sink logit joins the normaliser: rebase both terms on their larger
@@ -716,8 +754,15 @@ next_item:
 item_done: __attribute__((unused));
     if constexpr (PAIRED) {
         // the pair's light block: the slots are rewritten only after every wave is done
-        if (mblk != mrev) {
+        bool more = mblk != mrev;
+        if constexpr (SPLIT) more = which == 0 && pair_b > pair_la && pair_lb > 0;
+        if (more) {
             mblk = mrev;
+            if constexpr (SPLIT) {
+                which = 1;
+                seg0 = 0;
+                seg1 = pair_b - pair_la;
+            }
             __syncthreads();
             goto next_item;
         }
@@ -725,46 +770,73 @@ item_done: __attribute__((unused));
 }
 
 // The key-range split's second kernel: one workgroup per (query block, 32-channel block of O),
-// laid out like the attention kernel (one wave per 32 rows, the same lanes), merges the n_split
-// partial states in ascending order of key range.  The softmax over the union of the ranges is
+// laid out like the attention kernel (one wave per 32 rows, the same lanes), merges the partial
+// states of the ranges that cover the block, in ascending order of range.  The softmax over the
+// union of the ranges is
 //   O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,   M = max_i m_i   (base-2 units),
 // and LSE = (M + log2 of the denominator) ln 2, so the result does not depend on timing.  (Every
 // channel block's workgroup recomputes the row's weights from the same values, in the same
-// order; the first one writes the LSE.)
-template <int DQK, int DV>
+// order; the first one writes the LSE.)  Causal grids split pairs of blocks (n-1-j, j): ranges
+// [r L / n_split, (r + 1) L / n_split) of the pair's L = LA + LB tiles; block n-1-j takes the
+// ranges that start before LA, block j those that end after it.
+template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2)) void attn_split_merge(const AttnParams p) {
     constexpr int BM = TileCfg<DQK, DV>::BM;
+    constexpr int BN = TileCfg<DQK, DV>::BN;
     constexpr int NWAVES = BM / 32;
     constexpr int CBLK = DV / 32;
     constexpr int OWAVE = CBLK * 16 * 64;
     const int cb = blockIdx.x % CBLK;
-    const int item = blockIdx.x / CBLK;
+    const int unit = blockIdx.x / CBLK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int mblk = item % p.n_mblocks;
-    const int bh = item / p.n_mblocks;
+    int item, which = 0, mblk, bh, la = 0, len = 0;
+    if constexpr (CAUSAL) {
+        item = unit >> 1;
+        which = unit & 1;
+        const int per_head = (p.n_mblocks + 1) / 2;
+        const int mrev = item % per_head;
+        const int ma = p.n_mblocks - 1 - mrev;
+        if (which == 1 && ma == mrev) return;   // an odd count's middle block is one item
+        bh = item / per_head;
+        mblk = which ? mrev : ma;
+        la = split_causal_tiles<BM, BN>(ma, p.sk);
+        len = la + (ma != mrev ? split_causal_tiles<BM, BN>(mrev, p.sk) : 0);
+    } else {
+        item = unit;
+        mblk = item % p.n_mblocks;
+        bh = item / p.n_mblocks;
+    }
+    auto covers = [&](int r) __attribute__((always_inline)) {
+        if constexpr (!CAUSAL) return true;
+        return which == 0 ? r * len / p.n_split < la : (r + 1) * len / p.n_split > la;
+    };
     const int h = bh % p.hq;
     const int bb = bh / p.hq;
     const int my_row = mblk * BM + wave * 32 + col;
-    const int64_t slot0 = static_cast<int64_t>(item) * p.n_split * NWAVES + wave;
-    const f32x2* pml = reinterpret_cast<const f32x2*>(p.split_ml) + slot0 * 64 + lane;
+    auto slot = [&](int r) __attribute__((always_inline)) {
+        return ((static_cast<int64_t>(item) * p.n_split + r) * (CAUSAL ? 2 : 1) + which) * NWAVES + wave;
+    };
+    const f32x2* pml = reinterpret_cast<const f32x2*>(p.split_ml) + lane;
     float mmax = kNegInf;
-    for (int i = 0; i < p.n_split; ++i) mmax = fmaxf(mmax, pml[i * NWAVES * 64][0]);
+    for (int r = 0; r < p.n_split; ++r)
+        if (covers(r)) mmax = fmaxf(mmax, pml[slot(r) * 64][0]);
     f32x16 acc[1] = {f32x16{}};
     float lsum = 0.f;
-    for (int i = 0; i < p.n_split; ++i) {
-        const f32x2 ml = pml[i * NWAVES * 64];
+    for (int r = 0; r < p.n_split; ++r) {
+        if (!covers(r)) continue;
+        const f32x2 ml = pml[slot(r) * 64];
         const float w = ml[0] == kNegInf ? 0.f : fast_exp2(ml[0] - mmax);
         lsum = fmaf(w, ml[1], lsum);
-        const float* po = p.split_o + (slot0 + static_cast<int64_t>(i) * NWAVES) * OWAVE;
+        const float* po = p.split_o + slot(r) * OWAVE;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(po + ((cb * 4 + q4) * 64 + lane) * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[0][4 * q4 + r] = fmaf(w, x[r], acc[0][4 * q4 + r]);
+            for (int j = 0; j < 4; ++j) acc[0][4 * q4 + j] = fmaf(w, x[j], acc[0][4 * q4 + j]);
         }
     }
     if (my_row < p.sq) {
@@ -792,18 +864,22 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     // by (sequence, kv head), and pairing the 32-sequence workload's 8192-row grid cost +11%.
     const bool ext = p.window_left >= 0 || (!CAUSAL && p.window_right >= 0) || p.sinks != nullptr;
     if (p.n_split > 1) {
-        if constexpr (CAUSAL || VARLEN) {
+        if constexpr (VARLEN) {
             return hipErrorInvalidValue;
         } else {
             if (ext || p.split_ml == nullptr || p.split_o == nullptr) return hipErrorInvalidValue;
-            const int64_t nwg = blocks * p.n_split;
-            if (nwg > INT32_MAX || blocks * (DV / 32) > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>),
+            // units: query blocks, or causal pairs (n-1-j, j); the merge has one workgroup per
+            // (block, 32-channel block), two blocks per pair
+            const int64_t units = CAUSAL ? static_cast<int64_t>(p.b) * p.hq * ((p.n_mblocks + 1) / 2) : blocks;
+            const int64_t nwg = units * p.n_split;
+            const int64_t nmerge = units * (CAUSAL ? 2 : 1) * (DV / 32);
+            if (nwg > INT32_MAX || nmerge > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, CAUSAL, false, true>),
                                dim3(static_cast<unsigned>(nwg)), dim3(BM * 2), 0, stream, p);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((attn_split_merge<DQK, DV>), dim3(static_cast<unsigned>(blocks * (DV / 32))), dim3(BM * 2),
-                               0, stream, p);
+            hipLaunchKernelGGL((attn_split_merge<DQK, DV, CAUSAL>), dim3(static_cast<unsigned>(nmerge)), dim3(BM * 2), 0,
+                               stream, p);
             return hipGetLastError();
         }
     }
@@ -857,57 +933,121 @@ namespace {
 
 // rows per workgroup and the split kernel of a head-dim pair (nullptr: not built)
 template <int DQK, int DV>
-const void* split_kernel(int* bm) {
+const void* split_kernel(bool causal, int* bm) {
     *bm = TileCfg<DQK, DV>::BM;
-    return reinterpret_cast<const void*>(attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>);
+    return causal ? reinterpret_cast<const void*>(attn_fwd_bf16_kernel<DQK, DV, true, false, true, false, true>)
+                  : reinterpret_cast<const void*>(attn_fwd_bf16_kernel<DQK, DV, false, false, false, false, true>);
 }
 
-const void* split_kernel_for(int d_qk, int d_v, int* bm) {
-    if (d_qk == 32 && d_v == 32) return split_kernel<32, 32>(bm);
-    if (d_qk == 64 && d_v == 64) return split_kernel<64, 64>(bm);
-    if (d_qk == 128 && d_v == 128) return split_kernel<128, 128>(bm);
-    if (d_qk == 192 && d_v == 128) return split_kernel<192, 128>(bm);
+const void* split_kernel_for(int d_qk, int d_v, bool causal, int* bm) {
+    if (d_qk == 32 && d_v == 32) return split_kernel<32, 32>(causal, bm);
+    if (d_qk == 64 && d_v == 64) return split_kernel<64, 64>(causal, bm);
+    if (d_qk == 128 && d_v == 128) return split_kernel<128, 128>(causal, bm);
+    if (d_qk == 192 && d_v == 128) return split_kernel<192, 128>(causal, bm);
     return nullptr;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+constexpr int kSplitBN = 64;   // key tile of every TileCfg
+
+// Key tiles per range: non-causal, the ceil(sk / 64) tiles of every block (`shortest` as
+// `longest`); causal, the pair lengths LA + LB, the shortest and the longest.
+void split_lengths(int n_mblocks, int bm, int sk, bool causal, int* shortest, int* longest) {
+    if (!causal) {
+        *shortest = *longest = (sk + kSplitBN - 1) / kSplitBN;
+        return;
+    }
+    auto tiles = [&](int m) {
+        const int64_t keys = std::min<int64_t>(static_cast<int64_t>(m + 1) * bm, sk);
+        return static_cast<int>((keys + kSplitBN - 1) / kSplitBN);
+    };
+    int lo = INT32_MAX, hi = 0;
+    for (int j = 0; j < (n_mblocks + 1) / 2; ++j) {
+        const int ma = n_mblocks - 1 - j;
+        const int len = tiles(ma) + (ma != j ? tiles(j) : 0);
+        lo = std::min(lo, len);
+        hi = std::max(hi, len);
+    }
+    *shortest = n_mblocks > 0 ? lo : 0;
+    *longest = hi;
+}
+
 }  // namespace
 
 size_t attn_bf16_split_layout(int b, int hq, int sq, int d_qk, int d_v, int n_split, size_t offsets[2]) {
     int bm = 0;
-    if (split_kernel_for(d_qk, d_v, &bm) == nullptr || b < 0 || hq < 0 || sq < 0 || n_split < 1) return 0;
-    const size_t blocks = static_cast<size_t>(b) * hq * ((static_cast<size_t>(sq) + bm - 1) / bm);
+    if (split_kernel_for(d_qk, d_v, false, &bm) == nullptr || b < 0 || hq < 0 || sq < 0 || n_split < 1) return 0;
+    // two block slots per pair of blocks: the causal pairs (n-1-j, j), and at least the blocks
+    const size_t nmb = (static_cast<size_t>(sq) + bm - 1) / bm;
+    const size_t slots = static_cast<size_t>(b) * hq * 2 * ((nmb + 1) / 2);
     const size_t waves = static_cast<size_t>(bm / 32);
     offsets[0] = 0;
-    offsets[1] = round256(blocks * n_split * waves * 64 * 2 * sizeof(float));
-    return offsets[1] + round256(blocks * n_split * static_cast<size_t>(bm) * d_v * sizeof(float));
+    offsets[1] = round256(slots * n_split * waves * 64 * 2 * sizeof(float));
+    return offsets[1] + round256(slots * n_split * static_cast<size_t>(bm) * d_v * sizeof(float));
+}
+
+int attn_bf16_split_max(int sq, int sk, int d_qk, int d_v, bool causal) {
+    int bm = 0;
+    if (split_kernel_for(d_qk, d_v, causal, &bm) == nullptr || sq <= 0 || sk <= 0) return 0;
+    int shortest = 0, longest = 0;
+    split_lengths((sq + bm - 1) / bm, bm, sk, causal, &shortest, &longest);
+    return shortest;
 }
 
 hipError_t attn_bf16_split_plan(int b, int hq, int sq, int sk, int d_qk, int d_v, bool causal, int* n_split) {
     *n_split = 1;
     int bm = 0;
-    const void* kernel = split_kernel_for(d_qk, d_v, &bm);
-    if (kernel == nullptr || causal || b <= 0 || hq <= 0 || sq <= 0 || sk <= 0) return hipSuccess;
-    int slots = 0;
-    const hipError_t e = resident_groups(kernel, bm * 2, &slots);
+    const void* kernel = split_kernel_for(d_qk, d_v, causal, &bm);
+    if (kernel == nullptr || b <= 0 || hq <= 0 || sq <= 0 || sk <= 0) return hipSuccess;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    // Time in units of one key tile of one workgroup: rounds of resident workgroups times the
-    // tiles each runs, plus about two tiles per split workgroup for writing its partial and the
-    // merge.  A split must be predicted 10% faster, and each range must hold enough work that
-    // the merge kernel's launch and traffic stay small beside it: keys x (d_qk + d_v) >= 2^18,
-    // 1024 keys at d128 (measured on MI355X: the d128 8192^2 GQA 5:1 shape gains 12% at three
-    // ranges; a d32 2048^2 shape of 256 blocks loses at every split).
-    const int64_t blocks = static_cast<int64_t>(b) * hq * ((sq + bm - 1) / bm);
-    const int nt = (sk + 63) / 64;
-    auto rounds = [&](int64_t wgs) { return static_cast<double>((wgs + slots - 1) / slots); };
-    double best = rounds(blocks) * nt;
-    for (int s = 2; s <= 8 && static_cast<int64_t>(nt / s) * 64 * (d_qk + d_v) >= (int64_t(1) << 18); ++s) {
-        if (blocks * s > INT32_MAX) break;
-        const double cost = rounds(blocks * s) * (static_cast<double>(nt) / s + 2.0);
-        if (cost < 0.9 * best) {
-            best = cost;
+    if (cus <= 0) return hipSuccess;
+    // A model of the time in microseconds, calibrated on MI355X (d128, 8192^2, measured):
+    //  * k workgroups on a CU share its throughput, ~4.5 TFLOP/s per CU when every SIMD holds two
+    //    waves; one 4-wave workgroup alone (one wave per SIMD) runs at 0.87 of that;
+    //  * a split workgroup adds about one key tile of prologue and partial stores;
+    //  * the merge reads the fp32 partials at ~5 TB/s, plus ~3 us for its launch.
+    // It reproduces the measured choices: the GQA 5:1 non-causal shape (320 blocks) gains 12-13%
+    // at three ranges; the GQA 8:1 shapes, causal (256 pairs, one per CU) or not, lose at every
+    // split.  The split with the least predicted time is taken (the fewest ranges within 3% of
+    // it) if it beats the unsplit grid by 10%, and only with ranges of keys x (d_qk + d_v) >= 2^18,
+    // 1024 keys at d128, below which fixed costs dominate (a d32 2048^2 shape loses at every split).
+    // Causal grids split pairs of blocks (n-1-j, j), whose tile counts L = LA + LB are close to equal.
+    const int nmb = (sq + bm - 1) / bm;
+    const int64_t units = static_cast<int64_t>(b) * hq * (causal ? (nmb + 1) / 2 : nmb);
+    int shortest = 0, nt = 0;
+    split_lengths(nmb, bm, sk, causal, &shortest, &nt);
+    const double t_tile = static_cast<double>(bm) * kSplitBN * (d_qk + d_v) * 2.0 / 4.5e12 * 1e6;
+    const int waves = bm / 32;
+    auto cost = [&](int s) {
+        const int64_t k = (units * s + cus - 1) / cus;
+        const double tiles = static_cast<double>(nt) / s + (s > 1 ? 1.0 : 0.0);
+        double t = static_cast<double>(k) * tiles * t_tile / (k * waves < 8 ? 0.87 : 1.0);
+        if (s > 1) {
+            const double slots = causal ? units * (s + 1.0) : static_cast<double>(units) * s;
+            t += slots * bm * d_v * 4.0 / 5.0e12 * 1e6 + 3.0;
+        }
+        return t;
+    };
+    double costs[9] = {0};
+    int top = 1;
+    for (int s = 2; s <= 8 && s <= shortest && units * s <= INT32_MAX &&
+                    static_cast<int64_t>(nt / s) * kSplitBN * (d_qk + d_v) >= (int64_t(1) << 18);
+         ++s)
+        top = s;
+    double best = cost(1);
+    for (int s = 1; s <= top; ++s) {
+        costs[s] = cost(s);
+        best = std::min(best, costs[s]);
+    }
+    if (best >= 0.9 * costs[1]) return hipSuccess;
+    for (int s = 2; s <= top; ++s) {
+        if (costs[s] <= 1.03 * best) {
             *n_split = s;
+            break;
         }
     }
     return hipSuccess;

@@ -34,12 +34,12 @@ struct AttnParams {
     // -1 = unbounded on that side; per-query-head sink logits [hq] (nullptr = none)
     int window_left = -1, window_right = -1;
     const float* sinks = nullptr;
-    // key-range split (dense, non-causal): n_split workgroups per query block, each over a
-    // contiguous range of key tiles, leave their partial states in the workspace below; a
-    // second kernel merges them.  n_split == 1: no split.
+    // key-range split (dense grids): n_split workgroups per query block (causal: per pair of
+    // blocks), each over a contiguous range of key tiles, leave their partial states in the
+    // workspace below; a second kernel merges them.  n_split == 1: no split.
     int n_split = 1;
-    float* split_ml = nullptr;    // [blocks, n_split, waves, 64] (base-2 reference max, row sum)
-    float* split_o = nullptr;     // [blocks, n_split, waves, d_v / 32, 4, 64, 4] unnormalised O
+    float* split_ml = nullptr;    // [units, n_split, (causal: 2 blocks), waves, 64] (base-2 max, row sum)
+    float* split_o = nullptr;     // [units, n_split, (causal: 2), waves, d_v / 32, 4, 64, 4] unnormalised O
 };
 
 // Workgroups of `kernel` (launched with `threads` threads, no dynamic LDS) that the current
@@ -55,9 +55,12 @@ hipError_t launch_attn_fwd_bf16(const AttnParams& p, int d_qk, int d_v, bool cau
 // (each 256-byte aligned).  0 for an unsupported head-dim pair.
 size_t attn_bf16_split_layout(int b, int hq, int sq, int d_qk, int d_v, int n_split, size_t offsets[2]);
 
-// Key ranges per query block that balance the grid of this shape on the current device (1: the
-// unsplit grid already fills it, or the shape takes no split).
+// Key ranges per query block (causal: per pair of blocks) that balance the grid of this shape on
+// the current device (1: the unsplit grid already fills it, or the shape takes no split).
 hipError_t attn_bf16_split_plan(int b, int hq, int sq, int sk, int d_qk, int d_v, bool causal, int* n_split);
+
+// The largest n_split that leaves every range at least one key tile (0: no split possible).
+int attn_bf16_split_max(int sq, int sk, int d_qk, int d_v, bool causal);
 
 struct GateParams {
     const void* k;

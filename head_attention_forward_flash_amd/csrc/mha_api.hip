@@ -198,10 +198,12 @@ mha_status fwd_bf16(const void* q, mha_strides q_stride, const void* k, mha_stri
     if (n_split < 1 || n_split > kMaxSplit)
         return fail(MHA_ERR_VALUE, "n_split = %d: must be in [1, %d]", n_split, kMaxSplit);
     if (n_split > 1) {
-        if (causal) return fail(MHA_ERR_UNSUPPORTED, "the key-range split runs on non-causal attention only");
-        const int nt = (sk + 63) / 64;
-        if (n_split > nt)
-            return fail(MHA_ERR_VALUE, "n_split = %d exceeds the %d key tiles of 64 (sk = %d)", n_split, nt, sk);
+        if (window_left >= 0 || window_right >= 0 || sinks)
+            return fail(MHA_ERR_UNSUPPORTED, "the key-range split takes no window or sinks");
+        const int most = mha::attn_bf16_split_max(sq, sk, d_qk, d_v, causal != 0);
+        if (n_split > most)
+            return fail(MHA_ERR_VALUE, "n_split = %d exceeds the %d key tiles of 64 that the shortest %s holds (sk = %d)",
+                        n_split, most, causal ? "pair of causal query blocks" : "query block", sk);
         size_t off[2];
         const size_t need = mha::attn_bf16_split_layout(b, hq, sq, d_qk, d_v, n_split, off);
         if (!ws) return fail(MHA_ERR_WORKSPACE, "ws is NULL (need %zu bytes)", need);

@@ -108,28 +108,30 @@ mha_status mha_fwd_bf16(const void* q, mha_strides q_stride,
  * units idle: the per-rank shapes of "Tune MHA config & small-head pipeline
  * pathology" (The 8 remaining regressions: d128 8192^2 at TP8, hq8/hk1 and
  * hq5/hk1), whose 320-512 query blocks of 128 rows are one round of the
- * device or less.  Each workgroup runs keys [t0*64, t1*64) for its range of
- * the ceil(sk/64) key tiles (the ranges differ by at most one tile) and leaves
- * its fp32 state in the workspace; a second kernel on the same stream merges
- * the ranges in ascending order through the softmax identity over a union of
- * key sets,
+ * device or less.  Non-causal: each workgroup runs keys [t0*64, t1*64) for its
+ * range of the ceil(sk/64) key tiles (the ranges differ by at most one tile).
+ * Causal: the blocks are paired (n-1-j, j) as in the unsplit call, and the
+ * L = LA + LB key tiles of a pair (block n-1-j's, then block j's) are divided
+ * the same way, so a range may end in one block and go on in the other.  Each
+ * workgroup leaves an fp32 state per block it touches in the workspace; a
+ * second kernel on the same stream merges, per block, the ranges that cover it
+ * in ascending order through the softmax identity over a union of key sets,
  *   O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i,
  * which is the LSE merge of the same page's outputs (O, LSE).  The result is
  * deterministic but not bitwise the unsplit one: the probabilities are rounded
  * to bf16 against each range's own reference max and the sums run in another
  * order (both within the unsplit call's error bounds).
  *
- *   n_split  1 (exactly mha_fwd_bf16; ws ignored) to 16; above 1 only with
- *            causal = 0 (else MHA_ERR_UNSUPPORTED) and at most ceil(sk/64)
- *            (else MHA_ERR_VALUE)
+ *   n_split  1 (exactly mha_fwd_bf16; ws ignored) to 16, and at most the key
+ *            tiles of 64 of the shortest block (non-causal: ceil(sk/64)) or
+ *            pair of blocks (causal), else MHA_ERR_VALUE
  *   ws       device workspace of at least
  *            mha_fwd_bf16_split_workspace_bytes(b, hq, sq, d_qk, d_v, n_split)
  *            bytes, 256-byte aligned (else MHA_ERR_WORKSPACE).  Its contents
  *            need no initialisation and are scratch after the call; calls that
  *            overlap in time (another stream) need separate workspaces.
  * Everything else (shapes, layouts, errors) as mha_fwd_bf16.  Two kernels run
- * on `stream`: the attention kernel over b*hq*blocks*n_split workgroups, then
- * the merge over b*hq*blocks.
+ * on `stream`: the attention kernel, then the merge.
  */
 mha_status mha_fwd_bf16_split(const void* q, mha_strides q_stride,
                               const void* k, mha_strides k_stride,
@@ -140,19 +142,20 @@ mha_status mha_fwd_bf16_split(const void* q, mha_strides q_stride,
                               float softmax_scale, int causal,
                               int n_split, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace mha_fwd_bf16_split needs for n_split ranges: per query
- * block (128 rows; 256 for d_qk = 192), range and row an fp32 (max, sum) pair
- * for each of the row's two lanes and d_v fp32 partial outputs.  0 for
- * n_split <= 1, n_split above 16 or an unsupported head-dim pair. */
+/* Bytes of workspace mha_fwd_bf16_split needs for n_split ranges: for each
+ * pair of query blocks (128 rows; 256 for d_qk = 192; an odd count rounded up)
+ * two block slots, and per slot, range and row an fp32 (max, sum) pair for
+ * each of the row's two lanes and d_v fp32 partial outputs.  0 for n_split <=
+ * 1, n_split above 16 or an unsupported head-dim pair. */
 size_t mha_fwd_bf16_split_workspace_bytes(int b, int hq, int sq, int d_qk, int d_v, int n_split);
 
-/* The n_split that balances this shape's grid on the CURRENT device (its
- * compute units times the workgroups each holds): 1 when the unsplit grid
- * already fills it, for causal attention and for empty shapes; otherwise the
- * split (2..8) that a model of whole rounds of resident workgroups predicts at
- * least 10% faster, among those whose ranges keep keys * (d_qk + d_v) >= 2^18
- * (the merge kernel's cost stays small beside each range's work).  Shape errors as
- * mha_fwd_bf16; MHA_ERR_HIP if the device cannot be queried (then *n_split = 1). */
+/* The n_split for this shape on the CURRENT device (its compute units): 1 when
+ * the unsplit grid keeps the device busy and for empty shapes; otherwise the
+ * split (2..8) that a time model (workgroups per CU, a lone 4-wave workgroup at
+ * 0.87 of a CU's two-wave throughput, the merge's fp32 partial traffic)
+ * predicts at least 10% faster, among those whose ranges keep keys * (d_qk +
+ * d_v) >= 2^18 (fixed costs dominate below).  Shape errors as mha_fwd_bf16;
+ * MHA_ERR_HIP if the device cannot be queried (then *n_split = 1). */
 mha_status mha_fwd_bf16_split_plan(int b, int hq, int hk, int sq, int sk, int d_qk, int d_v, int causal,
                                    int* n_split);
 

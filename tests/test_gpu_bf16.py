@@ -109,6 +109,17 @@ def test_full_gqa5_d128_tp8_noncausal_sampled():
     _full_size_sampled("gqa5_d128_tp8_noncausal", [0, 2, 4], 128, 14)
 
 
+def test_full_gqa8_d128_tp8_causal_sampled():
+    # the same rank's causal prefill: 256 causal pairs, one workgroup per CU (unsplit)
+    _full_size_sampled("gqa8_d128_tp8_causal", [0, 5, 7], 128, 15)
+
+
+def test_full_gqa5_d128_tp8_causal_sampled():
+    # GQA 5:1 causal: 160 pairs, which the default call divides by key range (pairs of blocks
+    # whose ranges cross from one block into the other)
+    _full_size_sampled("gqa5_d128_tp8_causal", [0, 2, 4], 128, 16)
+
+
 def test_value_ones_gives_ones():
     # V = 1 everywhere: every output row is 1 whatever the scores, up to the bf16 rounding of
     # the probabilities fed to the P.V product and of O itself.

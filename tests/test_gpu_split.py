@@ -119,7 +119,6 @@ def test_split_against_unsplit_and_plan():
     n5 = mha.mha_fwd_bf16_split_plan(1, 5, 1, 8192, 8192, 128, 128, False)
     n8 = mha.mha_fwd_bf16_split_plan(1, 8, 1, 8192, 8192, 128, 128, False)
     assert n5 > 1 and n8 == 1, (n5, n8)
-    assert mha.mha_fwd_bf16_split_plan(1, 5, 1, 8192, 8192, 128, 128, True) == 1
     assert mha.mha_fwd_bf16_split_plan(1, 2, 2, 128, 128, 64, 64, False) == 1   # two key tiles
     # The same inputs through both kernels.  They differ in which reference max each probability
     # is rounded to bf16 against (the row sum adds the rounded values), so ln l moves by the
@@ -152,3 +151,70 @@ def test_split_on_strided_views():
     ob = out_buf.cpu()
     assert torch.all(ob[:, :, :2] == 0) and torch.all(ob[:, :, 5:] == 0)
     _check(q, k, v, ob[:, :, 2:5], lse.cpu(), scale_for(64), "strided split")
+
+
+CAUSAL_SPLIT_SHAPES = [
+    # b, hq, hk, sq, sk, d_qk, d_v, n_split
+    (1, 2, 1, 1000, 1000, 128, 128, 2),    # 8 blocks, 4 pairs of 18 tiles: ranges of 9 cross blocks
+    (1, 2, 1, 1000, 1000, 128, 128, 5),    # ranges of 3-4 tiles, some starting in diagonal tiles
+    (1, 2, 1, 1000, 1000, 128, 128, 16),   # the largest n_split the call takes: ranges of 1-2 tiles
+    (2, 3, 1, 520, 520, 64, 64, 3),        # 5 blocks: pairs (4, 0), (3, 1) and the middle block alone
+    (1, 2, 2, 900, 900, 192, 128, 4),      # 256-row blocks: pairs (3, 0), (2, 1)
+    (1, 4, 2, 300, 300, 32, 32, 4),        # d32: 3 blocks, the shortest pair 4 tiles
+    (1, 2, 1, 600, 900, 128, 128, 3),      # more keys than queries: keys past a block's rows unseen
+    (1, 2, 1, 900, 600, 128, 128, 3),      # fewer keys: the late blocks' tiles saturate at 10
+]
+
+
+@pytest.mark.parametrize("shape", CAUSAL_SPLIT_SHAPES,
+                         ids=[f"b{s[0]}h{s[1]}/{s[2]}q{s[3]}k{s[4]}d{s[5]}-{s[6]}x{s[7]}" for s in CAUSAL_SPLIT_SHAPES])
+def test_causal_split_matches_oracle(shape):
+    dev = require_gpu()
+    q, k, v = _inputs(shape, 3000 + sum(shape))
+    o, lse = _lib().mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=True, n_split=shape[-1])
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    b, hq = q.shape[0], q.shape[2]
+    scale = scale_for(shape[5])
+    for bb in range(b):
+        o_ref, l_ref = oracle_heads(q, k, v, list(range(hq)), None, scale=scale, causal=True, batch=bb)
+        assert_bf16_parity(to_np(o[bb]), o_ref, lse[bb].numpy().astype(np.float64), l_ref,
+                           f"causal split {shape} b={bb}")
+
+
+def test_causal_split_deterministic_and_spiked():
+    # a key ~150 above the rest inside the second block of a pair's sequence, and a rerun on a
+    # workspace filled with other bytes: the same bits
+    dev = require_gpu()
+    q = workloads.make_random((1, 1000, 2, 128), 81).float()
+    k = workloads.make_random((1, 1000, 1, 128), 82).float()
+    v = workloads.make_random((1, 1000, 1, 128), 83)
+    q[..., 0] = 1.0
+    k[0, 40, :, 0] = 150.0 * 128 ** 0.5     # in block 0, the second block of pair (7, 0)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    mha = _lib()
+    need = mha.mha_fwd_bf16_split_workspace_bytes(1, 2, 1000, 128, 128, 5)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=dev)
+    first = mha.mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=True, n_split=5, workspace=ws)
+    ws.fill_(0xA5)
+    again = mha.mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=True, n_split=5, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    o_ref, l_ref = oracle_heads(q, k, v, [0, 1], None, scale=scale_for(128), causal=True, batch=0)
+    assert_bf16_parity(to_np(first[0].cpu()[0]), o_ref, first[1].cpu()[0].numpy().astype(np.float64), l_ref,
+                       "causal split with a spike")
+
+
+def test_causal_split_plan():
+    mha = _lib()
+    # causal 8192^2 d128 per-rank shapes: hq8/hk1 makes 256 pairs, one per CU, where a lone
+    # workgroup already gets most of the CU (measured: every split slower) -> no split; hq5/hk1
+    # leaves 96 CUs idle and hq1 most of the device -> split
+    assert mha.mha_fwd_bf16_split_plan(1, 8, 1, 8192, 8192, 128, 128, True) == 1
+    assert mha.mha_fwd_bf16_split_plan(1, 5, 1, 8192, 8192, 128, 128, True) > 1
+    assert mha.mha_fwd_bf16_split_plan(1, 1, 1, 8192, 8192, 128, 128, True) > 1
+    # the d128 GQA 4096^2 causal shape: 512 pairs fill the device -> no split
+    assert mha.mha_fwd_bf16_split_plan(1, 32, 8, 4096, 4096, 128, 128, True) == 1
+    # the MLA shape and its TP8 share: 256-row blocks of 8 waves -> no split
+    assert mha.mha_fwd_bf16_split_plan(1, 128, 128, 8192, 8192, 192, 128, True) == 1
+    assert mha.mha_fwd_bf16_split_plan(1, 16, 16, 8192, 8192, 192, 128, True) == 1

@@ -104,6 +104,14 @@ WORKLOADS = {
     "gqa5_d128_tp8_noncausal": Workload(
         "gqa5_d128_tp8_noncausal", b=1, hq=5, hk=1, sq=8192, sk=8192, d_qk=128, d_v=128, causal=False,
         seed=116, description="b1 hq5 hk1 8192^2 d128 non-causal bf16 (one rank of 8-way head sharding)"),
+    # The same ranks' causal prefill: hq8/hk1 makes 256 causal pairs of query blocks, one
+    # workgroup per CU; hq5/hk1 makes 160, which the key-range split spreads over the device
+    "gqa8_d128_tp8_causal": Workload(
+        "gqa8_d128_tp8_causal", b=1, hq=8, hk=1, sq=8192, sk=8192, d_qk=128, d_v=128, causal=True,
+        seed=117, description="b1 hq8 hk1 8192^2 d128 causal bf16 (one rank of 8-way head sharding)"),
+    "gqa5_d128_tp8_causal": Workload(
+        "gqa5_d128_tp8_causal", b=1, hq=5, hk=1, sq=8192, sk=8192, d_qk=128, d_v=128, causal=True,
+        seed=118, description="b1 hq5 hk1 8192^2 d128 causal bf16 (one rank of 8-way head sharding)"),
     "fp8_long_h5": Workload(
         "fp8_long_h5", b=1, hq=5, hk=5, sq=65536, sk=65536, d_qk=128, d_v=128, causal=False,
         seed=109, fp8=True, k_bias_std=3.0,

@@ -104,11 +104,15 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 #ifndef MHA_EARLY_WIDE
 #define MHA_EARLY_WIDE 4
 #endif
+// REV: causal blocks in the lower half of their sequence run their key tiles downward (see the
+// main loop), for the head dims whose K/V per head outgrows an XCD's 4 MiB L2 on long sequences
+// (d192/d128: 5.2 MB at 8192 keys); the GQA shapes of the narrower heads share one kv head's K/V
+// between several query heads and keep it in L2 either way.
 template <int DQK, int DV> struct TileCfg;
-template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64, EARLY = 8; };
-template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, EARLY = 8; };
-template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, EARLY = MHA_EARLY_WIDE; };
-template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, EARLY = MHA_EARLY_WIDE; };
+template <> struct TileCfg<32, 32> { static constexpr int BM = 128, BN = 64, EARLY = 8; static constexpr bool REV = false; };
+template <> struct TileCfg<64, 64> { static constexpr int BM = 128, BN = 64, EARLY = 8; static constexpr bool REV = false; };
+template <> struct TileCfg<128, 128> { static constexpr int BM = 128, BN = 64, EARLY = MHA_EARLY_WIDE; static constexpr bool REV = false; };
+template <> struct TileCfg<192, 128> { static constexpr int BM = 256, BN = 64, EARLY = MHA_EARLY_WIDE; static constexpr bool REV = true; };
 
 // Key tiles of causal query block m (keys [0, min(sk, (m + 1) BM))).
 template <int BM, int BN>
@@ -306,6 +310,28 @@ next_item:
             }
         }
         const int ntiles = (kv_end + BN - 1) / BN;
+        // The loop runs over positions t0, t0 + 1, ... of the tile sequence.  With REV, causal
+        // blocks in the lower half of their sequence (block m with m < n - 1 - m, n blocks: the
+        // light block of each pair (n-1-j, j)) take their tiles downward, from the diagonal to
+        // tile t0 = 0.  The pairs of a head start together on one XCD: all of them read tile tau
+        // on the way up and tile L + 1 - tau on the way down (L + 2 tiles per pair), so the L2
+        // keeps the K/V tiles they share instead of each pair restarting at tile 0 at its own
+        // time.  The direction depends on the block and its sequence alone, so packed and dense
+        // calls, paired or not, sum every row in the same order.  Downward, position t is tile
+        // ntiles - 1 - t = (t ^ -1) + ntiles, and positions past the last tile map to negative
+        // tiles, whose buffer range is empty (tile_rsrc); block u of the positions is block
+        // (u ^ -2) + 2 ntiles of the key axis.
+        constexpr bool CAN_REV = TileCfg<DQK, DV>::REV && CAUSAL && !EXT && !SPLIT;
+        const bool rev = CAN_REV && mblk < (sq + BM - 1) / BM - 1 - mblk;
+        const int rev_x = rev ? -1 : 0, rev_c = rev ? ntiles : 0;
+        auto tile_at = [&](int t) __attribute__((always_inline)) {
+            if constexpr (!CAN_REV) return t;
+            else return (t ^ rev_x) + rev_c;
+        };
+        auto blk_at = [&](int u) __attribute__((always_inline)) {
+            if constexpr (!CAN_REV) return u;
+            else return (u ^ (rev_x * 2)) + rev_c * 2;
+        };
 
         // ---- DMA: lane l of a wave writes 16 bytes at block base + 16*l, and its global
         //      address decides what lands there.  The 16-byte chunks of a row are XOR-swizzled
@@ -337,19 +363,27 @@ next_item:
             const int r = pos / VROWB, pc = (pos % VROWB) / 16;
             vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
         }
+        // (with CAN_REV a tile index is taken as unsigned: the negative ones of a downward block
+        // start past any 32-bit slice)
         auto tile_rsrc = [&](const char* base, const View& vw, uint32_t slice, int t) __attribute__((always_inline)) {
-            const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
-            const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
-            return make_rsrc(left ? base + start : base, left);
+            if constexpr (CAN_REV) {
+                const uint64_t start = static_cast<uint64_t>(static_cast<uint32_t>(t)) * (BN * 2) * static_cast<uint64_t>(vw.ss);
+                const uint32_t left = start < slice ? static_cast<uint32_t>(slice - start) : 0u;
+                return make_rsrc(left ? base + start : base, left);
+            } else {
+                const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
+                const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
+                return make_rsrc(left ? base + start : base, left);
+            }
         };
         // past the last tile the buffer range is empty: nothing is read
         auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-            const auto r = tile_rsrc(kbase, p.kv, kslice, t);
+            const auto r = tile_rsrc(kbase, p.kv, kslice, tile_at(t));
 #pragma unroll
             for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
         };
         auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-            const auto r = tile_rsrc(vbase, p.vv, vslice, t);
+            const auto r = tile_rsrc(vbase, p.vv, vslice, tile_at(t));
 #pragma unroll
             for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
         };
@@ -417,9 +451,9 @@ next_item:
             }
         };
         // ---- scores of keys past sk, above the diagonal or outside the window become -inf
-        //      (block u = keys 32u ..)
+        //      (block u of the positions: keys 32 blk_at(u) ..)
         auto need_mask = [&](int u) __attribute__((always_inline)) {
-            const int key0 = u * 32;
+            const int key0 = blk_at(u) * 32;
             bool m = (key0 + 32 > sk) || (CAUSAL && key0 + 31 > wave_row0);
             if constexpr (EXT) {
                 m = m || (p.window_left >= 0 && key0 < wave_row0 + 31 - p.window_left) ||
@@ -430,7 +464,7 @@ next_item:
         auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int key = u * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+                const int key = blk_at(u) * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
                 bool out = key >= sk || (CAUSAL && key > my_row);
                 if constexpr (EXT) {
                     out = out || (p.window_left >= 0 && key < my_row - p.window_left) ||
@@ -500,7 +534,7 @@ next_item:
         const auto krs = make_rsrc(kbase, kslice);
         auto settle_global = [&](int u, PWords& pw, float bs) __attribute__((always_inline)) {
             if (__any(bs > lim)) {
-                const int key = u * 32 + col;
+                const int key = blk_at(u) * 32 + col;
                 const uint32_t row = key < sk ? static_cast<uint32_t>(key * p.kv.ss * 2) : kOutOfRange;
                 f32x16 st = f32x16{};
 #pragma unroll
@@ -663,34 +697,61 @@ next_item:
             f32x16 s0, s1;
             PWords p0, p1;
             KPre pre;
-            k_prefetch(k_slot(Zero{}), 0, pre);
-            qk_block(k_slot(Zero{}), 0, s0, pre);
-            if (need_mask(2 * t0)) mask_block(2 * t0, s0);
-            rebase(s0);                           // the row's first reference max
-            exp_pairs(s0, p0, IC<0>{}, Early{});
-            if constexpr (NARROW) l_run = block_sum(p0);
-            k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_t0
-            // Tiles up to `need` hold a key that some row of this wave sees; past them (the
-            // diagonal tiles of the rows above, or right of a window) the wave only keeps the
-            // ring's waits, barriers and its share of the DMA.  Wave-uniform.
-            int need = ntiles;
-            if constexpr (CAUSAL) need = min(ntiles, (wave_row0 + 31) / BN + 1);
-            if constexpr (EXT && !CAUSAL) {
-                if (p.window_right >= 0) need = min(ntiles, (wave_row0 + 31 + p.window_right) / BN + 1);
-            }
-            const int e = min(need, ntiles - 1);   // tiles run through iteration()
-            int t = t0;
-            for (; t + 2 <= e; t += 2) {
-                iteration(t, Zero{}, s0, s1, p0, p1, pre);
-                iteration(t + 1, One{}, s0, s1, p0, p1, pre);
-            }
-            const bool odd = t < e;
-            if (odd) iteration(t++, Zero{}, s0, s1, p0, p1, pre);
-            if (need == ntiles) {
-                if (odd) last(t, One{}, s0, s1, p0, p1, pre);
-                else last(t, Zero{}, s0, s1, p0, p1, pre);
+            if constexpr (!CAN_REV) {
+                k_prefetch(k_slot(Zero{}), 0, pre);
+                qk_block(k_slot(Zero{}), 0, s0, pre);
+                if (need_mask(2 * t0)) mask_block(2 * t0, s0);
+                rebase(s0);                           // the row's first reference max
+                exp_pairs(s0, p0, IC<0>{}, Early{});
+                if constexpr (NARROW) l_run = block_sum(p0);
+                k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_t0
+                // Tiles up to `need` hold a key that some row of this wave sees; past them (the
+                // diagonal tiles of the rows above, or right of a window) the wave only keeps the
+                // ring's waits, barriers and its share of the DMA.  Wave-uniform.
+                int need = ntiles;
+                if constexpr (CAUSAL) need = min(ntiles, (wave_row0 + 31) / BN + 1);
+                if constexpr (EXT && !CAUSAL) {
+                    if (p.window_right >= 0) need = min(ntiles, (wave_row0 + 31 + p.window_right) / BN + 1);
+                }
+                const int e = min(need, ntiles - 1);   // tiles run through iteration()
+                int t = t0;
+                for (; t + 2 <= e; t += 2) {
+                    iteration(t, Zero{}, s0, s1, p0, p1, pre);
+                    iteration(t + 1, One{}, s0, s1, p0, p1, pre);
+                }
+                const bool odd = t < e;
+                if (odd) iteration(t++, Zero{}, s0, s1, p0, p1, pre);
+                if (need == ntiles) {
+                    if (odd) last(t, One{}, s0, s1, p0, p1, pre);
+                    else last(t, Zero{}, s0, s1, p0, p1, pre);
+                } else {
+                    // tile t has parity (t - t0) & 1; the last tile issues no further DMA
+                    auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {
+                        using Cur = IC<decltype(par_c)::value>;
+                        using Nxt = IC<decltype(par_c)::value ^ 1>;
+                        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+                        __syncthreads();
+                        if (u + 1 < ntiles) {
+                            issue_k(u + 2, k_slot(Cur{}));
+                            issue_v(u + 1, v_slot(Nxt{}));
+                        }
+                    };
+                    bool par = odd;
+                    for (; t < ntiles; ++t) {
+                        if (par) drain(t, One{});
+                        else drain(t, Zero{});
+                        par = !par;
+                    }
+                }
             } else {
-                // tile t has parity (t - t0) & 1; the last tile issues no further DMA
+                // Causal, t0 = 0: every row sees key 0, so every wave runs to the last position.
+                // Upward, a wave stops computing after its diagonal tile and drains the rest;
+                // downward, it drains the tiles above its rows first and starts on block 0 of its
+                // diagonal tile, which holds a key that every row of the wave sees.  Either way
+                // each wave keeps one barrier per position.  Wave-uniform.
+                //
+                // a position the wave does not compute keeps the ring's wait, barrier and its share
+                // of the DMA; position t has parity (t - t0) & 1
                 auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {
                     using Cur = IC<decltype(par_c)::value>;
                     using Nxt = IC<decltype(par_c)::value ^ 1>;
@@ -701,11 +762,54 @@ next_item:
                         issue_v(u + 1, v_slot(Nxt{}));
                     }
                 };
-                bool par = odd;
-                for (; t < ntiles; ++t) {
-                    if (par) drain(t, One{});
+                // the wave's first block (block 0 of the tile at position u, ring slot par_c): its
+                // scores set the reference max
+                auto first_block = [&](int u, auto par_c) __attribute__((always_inline)) {
+                    using Cur = IC<decltype(par_c)::value>;
+                    k_prefetch(k_slot(Cur{}), 0, pre);
+                    qk_block(k_slot(Cur{}), 0, s0, pre);
+                    if (need_mask(2 * u)) mask_block(2 * u, s0);
+                    rebase(s0);
+                    exp_pairs(s0, p0, IC<0>{}, Early{});
+                    if constexpr (NARROW) l_run = block_sum(p0);
+                    k_prefetch(k_slot(Cur{}), 1, pre);   // the first region A starts on block 1
+                };
+                const int need = min(ntiles, (wave_row0 + 31) / BN + 1);
+                int t = t0;
+                for (const int first = rev ? t0 + ntiles - need : t0; t < first; ++t) {
+                    if ((t - t0) & 1) drain(t, One{});
                     else drain(t, Zero{});
-                    par = !par;
+                }
+                const int stop = rev ? ntiles : need;   // positions [t, stop) are computed
+                const int e = min(stop, ntiles - 1);    // through iteration()
+                bool odd = (t - t0) & 1;
+                if (!odd) {
+                    first_block(t, Zero{});
+                } else {
+                    first_block(t, One{});
+                    if (t < e) {
+                        iteration(t++, One{}, s0, s1, p0, p1, pre);
+                        odd = false;
+                    }
+                }
+                for (; t + 2 <= e; t += 2) {
+                    iteration(t, Zero{}, s0, s1, p0, p1, pre);
+                    iteration(t + 1, One{}, s0, s1, p0, p1, pre);
+                }
+                if (!odd && t < e) {
+                    iteration(t++, Zero{}, s0, s1, p0, p1, pre);
+                    odd = true;
+                }
+                if (stop == ntiles) {
+                    if (odd) last(t, One{}, s0, s1, p0, p1, pre);
+                    else last(t, Zero{}, s0, s1, p0, p1, pre);
+                } else {
+                    bool par = odd;
+                    for (; t < ntiles; ++t) {
+                        if (par) drain(t, One{});
+                        else drain(t, Zero{});
+                        par = !par;
+                    }
                 }
             }
         }

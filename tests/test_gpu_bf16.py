@@ -260,13 +260,14 @@ def test_late_score_spike_overflows_the_reference(dims):
     # query: against the reference max taken from the first block its probability overflows fp32
     # (2^216), so the block must take the rare path that moves the reference (for d128/d192 after
     # recomputing the block's scores from K in global memory) and redo its exponentials.  Keys
-    # before the spike keep their tiny weights relative to it.
+    # before the spike keep their tiny weights relative to it.  Key 3 is the same case for the
+    # light block of a causal pair, which runs its tiles downward and meets key 3 in its last block.
     dqk, dv = dims
     s = 300
     q = workloads.make_random((1, s, 2, dqk), 8100 + dqk, dtype=torch.float32, std=0.1)
     k = workloads.make_random((1, s, 2, dqk), 8101 + dqk, dtype=torch.float32, std=0.1)
     q[..., 0] = 1.0
-    for spike in (257, 100):
+    for spike in (257, 100, 3):
         k2 = k.clone()
         k2[0, spike, :, 0] = 150.0 * dqk ** 0.5
         v = workloads.make_random((1, s, 2, dv), 8102 + dqk)

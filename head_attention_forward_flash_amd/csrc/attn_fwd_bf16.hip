@@ -363,27 +363,34 @@ next_item:
             const int r = pos / VROWB, pc = (pos % VROWB) / 16;
             vgo[i] = static_cast<uint32_t>(r * p.vv.ss * 2 + ((pc ^ vswz(r)) * 16));
         }
-        // (with CAN_REV a tile index is taken as unsigned: the negative ones of a downward block
-        // start past any 32-bit slice)
-        auto tile_rsrc = [&](const char* base, const View& vw, uint32_t slice, int t) __attribute__((always_inline)) {
-            if constexpr (CAN_REV) {
-                const uint64_t start = static_cast<uint64_t>(static_cast<uint32_t>(t)) * (BN * 2) * static_cast<uint64_t>(vw.ss);
-                const uint32_t left = start < slice ? static_cast<uint32_t>(slice - start) : 0u;
-                return make_rsrc(left ? base + start : base, left);
-            } else {
-                const int64_t start = static_cast<int64_t>(t) * BN * vw.ss * 2;
-                const uint32_t left = start < static_cast<int64_t>(slice) ? static_cast<uint32_t>(slice - start) : 0u;
-                return make_rsrc(left ? base + start : base, left);
-            }
+        // A tile's buffer: its byte offset into the slice and the bytes left after it.  Per item,
+        // the number of tiles that start inside a slice (a slice holds less than 4 GiB) and the
+        // tile stride; tile t < that number then starts at t * stride < 2^32, so the loop needs
+        // 32-bit scalar arithmetic only (the scalar unit has no unsigned 64-bit less-than).  A
+        // tile index is taken as unsigned: the negative ones of a downward block (CAN_REV) start
+        // past any slice.
+        auto tile_geom = [](const View& vw, uint32_t slice, uint32_t& stride, uint32_t& tiles) __attribute__((always_inline)) {
+            const uint64_t b = static_cast<uint64_t>(BN * 2) * static_cast<uint64_t>(vw.ss);
+            stride = static_cast<uint32_t>(b);
+            tiles = slice == 0 ? 0u : b >= slice ? 1u : (slice - 1) / stride + 1;
+        };
+        uint32_t kstride, ktiles, vstride, vtiles;
+        tile_geom(p.kv, kslice, kstride, ktiles);
+        tile_geom(p.vv, vslice, vstride, vtiles);
+        auto tile_rsrc = [&](const char* base, uint32_t slice, uint32_t stride, uint32_t tiles, int t) __attribute__((always_inline)) {
+            const uint32_t tu = static_cast<uint32_t>(t);
+            const bool inside = tu < tiles;
+            const uint32_t start = tu * stride;
+            return make_rsrc(inside ? base + start : base, inside ? slice - start : 0u);
         };
         // past the last tile the buffer range is empty: nothing is read
         auto issue_k = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-            const auto r = tile_rsrc(kbase, p.kv, kslice, tile_at(t));
+            const auto r = tile_rsrc(kbase, kslice, kstride, ktiles, tile_at(t));
 #pragma unroll
             for (int i = 0; i < KDMA; ++i) buffer_load_lds_b128(r, slot + (wave * KDMA + i) * 1024, kgo[i]);
         };
         auto issue_v = [&](int t, uint8_t* slot) __attribute__((always_inline)) {
-            const auto r = tile_rsrc(vbase, p.vv, vslice, tile_at(t));
+            const auto r = tile_rsrc(vbase, vslice, vstride, vtiles, tile_at(t));
 #pragma unroll
             for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
         };

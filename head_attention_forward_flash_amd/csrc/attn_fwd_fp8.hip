@@ -228,10 +228,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         vgo[i] = static_cast<uint32_t>(r * VROWB + (pc ^ vswz(r)) * 16);
     }
     // (the descriptor's fields go through readfirstlane: a descriptor the compiler cannot prove
-    // uniform would wrap every DMA instruction in a loop over lanes)
+    // uniform would wrap every DMA instruction in a loop over lanes).  A slice holds nk * BM / BN
+    // tiles; the range test is on the tile index, so that the bytes left are not a saturating
+    // subtraction, which only the vector unit has.
+    const uint32_t slice_tiles = static_cast<uint32_t>(p.nk) * (BM / BN);
     auto tile_rsrc = [&](const uint8_t* base, uint32_t slice, uint32_t rowb, int t) __attribute__((always_inline)) {
         const uint32_t start = static_cast<uint32_t>(t) * BN * rowb;
-        const uint32_t left = start < slice ? slice - start : 0u;
+        const uint32_t left = static_cast<uint32_t>(t) < slice_tiles ? slice - start : 0u;
         const uint64_t addr = uniform_u64(reinterpret_cast<uint64_t>(base) + (left ? start : 0u));
         return make_rsrc(reinterpret_cast<const void*>(addr), static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(left)));
     };

@@ -92,7 +92,7 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 }
 
 template <int D, bool CAUSAL, bool MX>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
     constexpr int NWAVES = NTHREADS / 64;
     constexpr int KROWB = D;                  // bytes per K8 row
     constexpr int VROWB = D * 2;              // bytes per widened V row
@@ -121,19 +121,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         else return v_lds1;
     };
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 31;
-    const int half = lane >> 5;
-
+    // ---- workgroup -> (batch, head, query block); consecutive logical ids stay on one XCD.
+    //      Causal grids pair the query blocks of a head (as the bf16 kernel does): a workgroup
+    //      takes block n-1-j and then block j, so every workgroup does the same work.
     const int nwg = gridDim.x;
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
     const int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
-    const int mrev = lid % p.n_mblocks;
-    const int bh = lid / p.n_mblocks;
-    const int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;
+    const int per_head = CAUSAL ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
+    const int mrev = lid % per_head;
+    const int bh = lid / per_head;
+    int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: the heavy block first
     const int h = bh % p.hq;
     const int bb = bh / p.hq;
     const int g = h / p.group;
@@ -145,12 +143,34 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
     const auto qrs = make_rsrc(p.q + static_cast<int64_t>(bh) * qslice, qslice);
     const uint8_t* kbase = p.k + static_cast<int64_t>(bg) * kslice;
     const uint8_t* vbase = p.v + static_cast<int64_t>(bg) * vslice;
-    const float q_scale = MX ? 1.f : p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
     const float* k_scale = MX ? nullptr : p.k_scale + static_cast<int64_t>(bg) * p.nk;
     const float* v_scale = MX ? nullptr : p.v_scale + static_cast<int64_t>(bg) * p.nk;
     // MXFP8 exponents: 4 bytes per row (one per 32 channels), rows padded like the codes
     const uint32_t exp_slice = static_cast<uint32_t>(p.nk) * BM * EB;
     const auto kers = make_rsrc(MX ? p.k_exps + static_cast<int64_t>(bg) * exp_slice : nullptr, MX ? exp_slice : 0u);
+
+    // LDS starts as zeros so that any row the DMA does not fill holds finite values
+    for (int i = threadIdx.x; i < KTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
+    }
+    for (int i = threadIdx.x; i < VTILE / 16; i += NTHREADS) {
+        reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
+        reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+
+next_item:
+    // A pair's second block passes the lane index through an empty asm statement: nothing derived
+    // from it is then hoisted out of the loop over the pair, where it would stay live across every
+    // tile and crowd the tile loop's registers.
+    {
+    int tid = threadIdx.x;
+    if constexpr (CAUSAL) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
 
     const int wave_row0 = mblk * BM + wave * 32;
     const int my_row = wave_row0 + col;
@@ -167,6 +187,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         const u32x4 b = buffer_load_b128(qrs, off + (MX ? 32 : 16)) ^ qsign;
         qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
+    const float q_scale = MX ? 1.f : p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
     const float cq = q_scale * fabsf(p.scale_log2);   // base-2 factor of this block's scores, >= 0
     // MXFP8: the E8M0 byte of each k-step's 32 channels of this lane's query, in bits 0-7
     uint32_t qe[KS];
@@ -249,16 +270,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
 #pragma unroll
         for (int i = 0; i < VDMA; ++i) buffer_load_lds_b128(r, slot + (wave * VDMA + i) * 1024, vgo[i]);
     };
-
-    for (int i = tid; i < KTILE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
-    }
-    for (int i = tid; i < VTILE / 16; i += NTHREADS) {
-        reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
-        reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
-    }
-    __syncthreads();
 
     f32x16 oacc[CBLK];
 #pragma unroll
@@ -549,16 +560,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
         exp_pairs(s0, sc, p0, IC<0>{}, Early{});
         if constexpr (NARROW) l_run = block_sum(p0) * sc.inv_sv;
         k_prefetch(k_slot(Zero{}), 1, pre);   // the first region A starts on block 1 of K_0
+        // Tiles up to `need` hold a key that some row of this wave sees; past them (the diagonal
+        // tiles of the rows above) the wave only keeps the ring's waits, barriers and its share
+        // of the DMA.  Wave-uniform.
+        int need = ntiles;
+        if constexpr (CAUSAL) need = min(ntiles, (wave_row0 + 31) / BN + 1);
+        const int e = min(need, ntiles - 1);   // tiles run through iteration()
         int t = 0;
-        for (; t + 2 < ntiles; t += 2) {
+        for (; t + 2 <= e; t += 2) {
             iteration(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
             iteration(t + 1, One{}, s0, s1, p0, p1, sc, ke, pre);
         }
-        if (t + 1 < ntiles) {
-            iteration(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
-            last(t + 1, One{}, s0, s1, p0, p1, sc, ke, pre);
+        const bool odd = t < e;
+        if (odd) iteration(t++, Zero{}, s0, s1, p0, p1, sc, ke, pre);
+        if (need == ntiles) {
+            if (odd) last(t, One{}, s0, s1, p0, p1, sc, ke, pre);
+            else last(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
         } else {
-            last(t, Zero{}, s0, s1, p0, p1, sc, ke, pre);
+            // tile t has parity t & 1; the last tile issues no further DMA
+            auto drain = [&](int u, auto par_c) __attribute__((always_inline)) {
+                using Cur = IC<decltype(par_c)::value>;
+                using Nxt = IC<decltype(par_c)::value ^ 1>;
+                __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+                __syncthreads();
+                if (u + 1 < ntiles) {
+                    issue_k(u + 2, k_slot(Cur{}));
+                    issue_v(u + 1, v_slot(Nxt{}));
+                }
+            };
+            bool par = odd;
+            for (; t < ntiles; ++t) {
+                if (par) drain(t, One{});
+                else drain(t, Zero{});
+                par = !par;
+            }
         }
     }
 
@@ -572,13 +607,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_fp8_kernel(const Fp8Attn
             p.lse[(static_cast<int64_t>(bb) * p.hq + h) * p.sq + my_row] = lse;
         }
     }
+    }
+    if constexpr (CAUSAL) {
+        // the pair's light block: the slots are rewritten only after every wave is done
+        if (mblk != mrev) {
+            mblk = mrev;
+            __syncthreads();
+            goto next_item;
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_fp8(const Fp8AttnParams& p, int d, bool causal, hipStream_t stream) {
     if (d != 64 && d != 128) return hipErrorInvalidValue;
-    const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * p.n_mblocks;
+    // causal grids pair query blocks n-1-j and j in one workgroup
+    const int64_t nwg = static_cast<int64_t>(p.b) * p.hq * (causal ? (p.n_mblocks + 1) / 2 : p.n_mblocks);
     if (nwg == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(nwg));
     const bool mx = p.q_exps != nullptr;

@@ -135,6 +135,15 @@ def test_full_fp8_workload_sampled_heads():
     _check_attention(q, k, v, mu, w.causal, "fp8 workload", heads=[0, 7, 15])
 
 
+def test_full_fp8_workload_causal_sampled_heads():
+    # The same inputs under the causal mask: 32 query blocks per head run as 16 workgroups that
+    # each take blocks n-1-j and j; every row of three heads, i.e. every pair of those heads
+    w = workloads.WORKLOADS["fp8_ksmooth_d128"]
+    q, k, v = workloads.make_qkv(w)
+    mu = _oracle_mu(k)
+    _check_attention(q, k, v, mu, True, "fp8 workload causal", heads=[0, 7, 15])
+
+
 def test_long_context_fp8_sampled():
     # b1 h5 65536^2: 512 K/V scale blocks per head; sampled rows of the first and last head
     w = workloads.WORKLOADS["fp8_long_h5"]

@@ -42,6 +42,11 @@ SMALL_SHAPES = [
     (2, 2, 1, 333, 200, 128, 128),
     (1, 2, 2, 190, 190, 192, 128),
     (1, 3, 3, 129, 65, 192, 128),
+    # several 256-row blocks: causal pairs whose light block runs its tiles downward, with a
+    # ragged last block, more keys than queries and fewer
+    (1, 2, 2, 700, 700, 192, 128),
+    (1, 2, 1, 600, 800, 192, 128),
+    (2, 2, 2, 800, 520, 192, 128),
 ]
 
 

@@ -123,6 +123,16 @@ def test_ragged_gqa(causal, d):
     _check_attention(q, k, v, _oracle_mu(k), causal, f"ragged gqa d{d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", [(700, 520), (520, 700), (900, 900)], ids=["q700k520", "q520k700", "q900k900"])
+def test_causal_pairs_ragged(shape, d):
+    # causal grids with 5 to 8 query blocks, paired (n-1-j, j) with a middle block left over when
+    # n is odd, ragged last blocks, and more or fewer keys than queries
+    sq, sk = shape
+    q, k, v = _inputs(1, sq, sk, 2, 1, d, 900 + d + sq)
+    _check_attention(q, k, v, _oracle_mu(k), True, f"causal pairs d{d} {sq}x{sk}")
+
+
 def test_no_smoothing():
     q, k, v = _inputs(1, 256, 384, 2, 2, 128, 700, bias_std=0.0)
     _check_attention(q, k, v, None, False, "no smoothing")

@@ -71,21 +71,24 @@ def test_unequal_query_and_key_lengths(dims):
         assert torch.all(torch.isneginf(lse[:, r0:r0 + lens_q[3]]))
 
 
-def test_loose_maximum_and_equal_lengths_match_dense():
+@pytest.mark.parametrize("dims", [(128, 128, 333), (192, 128, 700)], ids=["d128", "d192"])
+def test_loose_maximum_and_equal_lengths_match_dense(dims):
     # equal lengths: the packed call must reproduce the dense call bit for bit, also when
-    # max_seqlen is larger than every sequence
+    # max_seqlen is larger than every sequence (the packed grid then pairs other blocks: at d192
+    # the light blocks' downward order must follow the sequence, not the grid)
     import head_attention_forward_flash_amd as mha
     dev = require_gpu()
-    b, s, hq, hk, d = 3, 333, 4, 2, 128
+    d, dv, s = dims
+    b, hq, hk = 3, 4, 2
     q = workloads.make_random((b, s, hq, d), 4200)
     k = workloads.make_random((b, s, hk, d), 4201)
-    v = workloads.make_random((b, s, hk, d), 4202)
+    v = workloads.make_random((b, s, hk, dv), 4202)
     for causal in (False, True):
-        od, ld = mha.mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=causal)
-        ov, lv = _run(q.reshape(b * s, hq, d), k.reshape(b * s, hk, d), v.reshape(b * s, hk, d), [s] * b,
+        od, ld = mha.mha_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), causal=causal, n_split=1)
+        ov, lv = _run(q.reshape(b * s, hq, d), k.reshape(b * s, hk, d), v.reshape(b * s, hk, dv), [s] * b,
                       [s] * b, causal, d ** -0.5, max_q=1000, max_k=1000)
         torch.cuda.synchronize()
-        assert torch.equal(ov.reshape(b, s, hq, d), od.cpu())
+        assert torch.equal(ov.reshape(b, s, hq, dv), od.cpu())
         assert torch.equal(lv.reshape(hq, b, s).permute(1, 0, 2), ld.cpu())
 
 

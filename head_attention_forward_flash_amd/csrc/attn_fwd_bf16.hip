@@ -104,6 +104,10 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
 #ifndef MHA_EARLY_WIDE
 #define MHA_EARLY_WIDE 4
 #endif
+// Query heads per workgroup for d128 under GQA (see HPW below); 1 turns it off
+#ifndef MHA_HEADS_PER_WG
+#define MHA_HEADS_PER_WG 2
+#endif
 // REV: causal blocks in the lower half of their sequence run their key tiles downward (see the
 // main loop), for the head dims whose K/V per head outgrows an XCD's 4 MiB L2 on long sequences
 // (d192/d128: 5.2 MB at 8192 keys); the GQA shapes of the narrower heads share one kv head's K/V
@@ -125,15 +129,21 @@ __host__ __device__ __forceinline__ int split_causal_tiles(int m, int sk) {
 // the sequence) and per-head sink logits.  SPLIT: grids that would underfill the device give each
 // query block (non-causal) or each pair of causal blocks (n-1-j, j) p.n_split workgroups, each
 // over one contiguous range of the key tiles, which leave partial states for attn_split_merge.
-template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT>
+// HPW: query heads per workgroup.  Under GQA the query heads of one kv head read the same K/V
+// tiles; a workgroup of HPW x (BM / 32) waves takes the same BM rows of HPW such heads, so each
+// tile that the DMA brings into LDS serves HPW times the rows (each wave's rows, diagonal and
+// registers stay as with one head).  Dense grids only.
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT, int HPW = 1>
 // Windows and sinks at d64 run four workgroups per CU (128 VGPRs): a 128-token window gives a
 // workgroup a few tiles, so the grid is bound by latency more than by issue (measured: the
 // GPT-OSS-like window layer 78.6 -> 71.9 us; the full causal layer with sinks unchanged; the
 // paired d64 kernel spills in its loop at 128 VGPRs and loses 13%, so it keeps three).
-__global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2), (EXT && DQK <= 64 ? 4 : 2)) void attn_fwd_bf16_kernel(const AttnParams p) {
-    constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per workgroup
-    constexpr int NTHREADS = BM * 2;                   // one wave per 32 rows
+__global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2 * HPW), (EXT && DQK <= 64 ? 4 : HPW > 1 ? 1 : 2)) void attn_fwd_bf16_kernel(const AttnParams p) {
+    constexpr int BM = TileCfg<DQK, DV>::BM;           // query rows per head and workgroup
+    constexpr int RWAVES = BM / 32;                    // one wave per 32 rows of a head
+    constexpr int NTHREADS = BM * 2 * HPW;
     constexpr int NWAVES = NTHREADS / 64;
+    static_assert(HPW == 1 || (!VARLEN && !EXT && !SPLIT), "several heads per workgroup on dense grids only");
     constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
     constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
     constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
@@ -229,9 +239,10 @@ next_item:
     const int col = lane & 31;     // query column of this lane in S^T / O^T
     const int half = lane >> 5;    // which half of the wave
     {
-        const int h = bh % p.hq;
-        const int bb = bh / p.hq;
-        const int g = h / p.group;
+        // bh: (batch, head) or, with HPW > 1, (batch, group of HPW heads); the wave's head
+        const int h = HPW == 1 ? bh % p.hq : (bh % (p.hq / HPW)) * HPW + wave / RWAVES;
+        const int bb = HPW == 1 ? bh / p.hq : bh / (p.hq / HPW);
+        const int g = h / p.group;   // the same for every wave: HPW divides the group
 
         // ---- this workgroup's sequence: the whole batch row, or (varlen) packed tokens
         //      [q0, q0 + sq) and [k0, k0 + sk) of the token axis.  Offsets are clamped to the
@@ -267,7 +278,7 @@ next_item:
         const char* vbase = static_cast<const char*>(p.v) + 2 * (vrow0 + g * p.vv.sh);
         const auto qrs = make_rsrc(qbase, qslice);
 
-        const int wave_row0 = mblk * BM + wave * 32;
+        const int wave_row0 = mblk * BM + (HPW == 1 ? wave : wave % RWAVES) * 32;
         const int my_row = wave_row0 + col;
 
         // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[my_row][kk*16 + half*8 .. +8]
@@ -1005,6 +1016,24 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
         return hipGetLastError();
     }
     bool paired = CAUSAL && p.n_mblocks > 1;
+    // d128 under GQA: two query heads per workgroup, when the grid still fills the device
+    if constexpr (DQK == 128 && DV == 128 && !VARLEN && MHA_HEADS_PER_WG > 1) {
+        constexpr int H = MHA_HEADS_PER_WG;
+        if (p.group % H == 0) {
+            const int64_t per_head = paired ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
+            const int64_t nwg = static_cast<int64_t>(p.b) * (p.hq / H) * per_head;
+            int groups = 0;
+            const auto kernel = paired ? attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, CAUSAL, false, false, H>
+                                       : attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, false, false, false, H>;
+            const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2 * H, &groups);
+            if (e != hipSuccess) return e;
+            if (nwg >= groups) {
+                if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+                hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nwg)), dim3(BM * 2 * H), 0, stream, p);
+                return hipGetLastError();
+            }
+        }
+    }
     if (paired && VARLEN) {
         int groups = 0;
         const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false, false>;

@@ -61,6 +61,22 @@ def test_multi_tile_ragged(shape, causal):
     _check_all(q, k, v, causal, f"shape={shape} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq, sk", [(200, 200), (200, 333), (300, 160)])
+def test_two_heads_per_workgroup(sq, sk, causal):
+    # d128 GQA grids that still fill the device with two query heads per workgroup (hq 512 over
+    # hk 256: 256 workgroups) take the packed kernel: waves 0-3 of a workgroup serve head 2i,
+    # waves 4-7 head 2i+1, on the same K/V tiles; ragged blocks, more and fewer keys than queries
+    q = workloads.make_random((1, sq, 512, 128), 4300 + sq + int(causal))
+    k = workloads.make_random((1, sk, 256, 128), 4301 + sk)
+    v = workloads.make_random((1, sk, 256, 128), 4302 + sk)
+    o, lse = _run(q, k, v, causal)
+    heads = list(range(0, 512, 37)) + [1, 2, 3, 510, 511]
+    o_ref, l_ref = oracle_heads(q, k, v, heads, None, scale=scale_for(128), causal=causal, batch=0)
+    assert_bf16_parity(to_np(o[0][:, heads]), o_ref, lse[0][heads].numpy().astype(np.float64), l_ref,
+                       f"two heads per workgroup {sq}x{sk} causal={causal}")
+
+
 def _full_size_sampled(name, heads, nrows, seed):
     """The full-size launch: many seeded rows (and the block edges) of a few heads, plus one
     seeded row of every (batch, head, 128-row block), i.e. of every workgroup."""

@@ -65,8 +65,9 @@ def test_multi_tile_ragged(shape, causal):
 @pytest.mark.parametrize("sq, sk", [(200, 200), (200, 333), (300, 160)])
 def test_two_heads_per_workgroup(sq, sk, causal):
     # d128 GQA grids that still fill the device with two query heads per workgroup (hq 512 over
-    # hk 256: 256 workgroups) take the packed kernel: waves 0-3 of a workgroup serve head 2i,
-    # waves 4-7 head 2i+1, on the same K/V tiles; ragged blocks, more and fewer keys than queries
+    # hk 256: 256 workgroups of 8 waves) take the packed kernel: waves 0-3 of a workgroup serve
+    # head 2i, waves 4-7 head 2i+1, on the same K/V tiles.  Ragged blocks, more and fewer keys
+    # than queries.
     q = workloads.make_random((1, sq, 512, 128), 4300 + sq + int(causal))
     k = workloads.make_random((1, sk, 256, 128), 4301 + sk)
     v = workloads.make_random((1, sk, 256, 128), 4302 + sk)

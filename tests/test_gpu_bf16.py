@@ -78,6 +78,20 @@ def test_two_heads_per_workgroup(sq, sk, causal):
                        f"two heads per workgroup {sq}x{sk} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_heads_per_workgroup_batched(causal):
+    # the packed kernel over two batches (hq 256 over hk 128: 256 workgroups), every batch checked
+    q = workloads.make_random((2, 200, 256, 128), 4400 + int(causal))
+    k = workloads.make_random((2, 260, 128, 128), 4401)
+    v = workloads.make_random((2, 260, 128, 128), 4402)
+    o, lse = _run(q, k, v, causal)
+    heads = list(range(0, 256, 29)) + [1, 254, 255]
+    for bb in range(2):
+        o_ref, l_ref = oracle_heads(q, k, v, heads, None, scale=scale_for(128), causal=causal, batch=bb)
+        assert_bf16_parity(to_np(o[bb][:, heads]), o_ref, lse[bb][heads].numpy().astype(np.float64), l_ref,
+                           f"two heads per workgroup b={bb} causal={causal}")
+
+
 def _full_size_sampled(name, heads, nrows, seed):
     """The full-size launch: many seeded rows (and the block edges) of a few heads, plus one
     seeded row of every (batch, head, 128-row block), i.e. of every workgroup."""

@@ -65,6 +65,10 @@ constexpr float kSumLimit = 256.0f;
 #ifndef MHA_FP8_EARLY
 #define MHA_FP8_EARLY 5
 #endif
+// Query blocks per workgroup on non-causal d128 grids (see RB below); 1 turns it off
+#ifndef MHA_FP8_BLOCKS_PER_WG
+#define MHA_FP8_BLOCKS_PER_WG 2
+#endif
 constexpr int EARLY = MHA_FP8_EARLY;
 template <int N> using IC = std::integral_constant<int, N>;
 constexpr float kMinFactor = 1.17549435e-38f;   // FLT_MIN
@@ -91,9 +95,13 @@ __device__ __forceinline__ void sched_region(std::integer_sequence<int, I...>) {
     (sched_slot<I, VMEM, DS_SLOTS, DS_PER, VALU_SLOTS, VALU_PER>(), ...);
 }
 
-template <int D, bool CAUSAL, bool MX>
-__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
-    constexpr int NWAVES = NTHREADS / 64;
+// RB: query blocks of one head per workgroup.  Non-causal grids that still fill the device give a
+// workgroup of RB x 4 waves RB consecutive blocks, which share every K/V tile the DMA brings in
+// (each wave's rows and registers stay as with one block).
+template <int D, bool CAUSAL, bool MX, int RB = 1>
+__global__ __launch_bounds__(NTHREADS * RB, D == 64 ? 3 : RB > 1 ? 1 : 2) void attn_fwd_fp8_kernel(const Fp8AttnParams p) {
+    static_assert(RB == 1 || !CAUSAL, "causal grids pair blocks instead");
+    constexpr int NWAVES = NTHREADS * RB / 64;
     constexpr int KROWB = D;                  // bytes per K8 row
     constexpr int VROWB = D * 2;              // bytes per widened V row
     constexpr int KTILE = BN * KROWB;
@@ -128,10 +136,10 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void attn_fwd_fp8_kernel
     const int nwg8 = nwg & ~7;
     const int pid = blockIdx.x;
     const int lid = pid < nwg8 ? (pid & 7) * (nwg8 >> 3) + (pid >> 3) : pid;
-    const int per_head = CAUSAL ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
+    const int per_head = CAUSAL ? (p.n_mblocks + 1) / 2 : (p.n_mblocks + RB - 1) / RB;
     const int mrev = lid % per_head;
     const int bh = lid / per_head;
-    int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev;   // causal: the heavy block first
+    int mblk = CAUSAL ? (p.n_mblocks - 1 - mrev) : mrev * RB;   // causal: the heavy block first
     const int h = bh % p.hq;
     const int bb = bh / p.hq;
     const int g = h / p.group;
@@ -150,11 +158,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void attn_fwd_fp8_kernel
     const auto kers = make_rsrc(MX ? p.k_exps + static_cast<int64_t>(bg) * exp_slice : nullptr, MX ? exp_slice : 0u);
 
     // LDS starts as zeros so that any row the DMA does not fill holds finite values
-    for (int i = threadIdx.x; i < KTILE / 16; i += NTHREADS) {
+    for (int i = threadIdx.x; i < KTILE / 16; i += NTHREADS * RB) {
         reinterpret_cast<u32x4*>(k_lds0)[i] = u32x4{0, 0, 0, 0};
         reinterpret_cast<u32x4*>(k_lds1)[i] = u32x4{0, 0, 0, 0};
     }
-    for (int i = threadIdx.x; i < VTILE / 16; i += NTHREADS) {
+    for (int i = threadIdx.x; i < VTILE / 16; i += NTHREADS * RB) {
         reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0, 0, 0, 0};
         reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0, 0, 0, 0};
     }
@@ -172,7 +180,10 @@ next_item:
     const int col = lane & 31;
     const int half = lane >> 5;
 
-    const int wave_row0 = mblk * BM + wave * 32;
+    // the wave's query block (RB > 1: the workgroup's blocks mblk, mblk + 1, ...; one past the
+    // last block holds no rows: its Q reads as zeros and nothing of it is stored)
+    const int wblk = RB == 1 ? mblk : mblk + wave / 4;
+    const int wave_row0 = wblk * BM + (RB == 1 ? wave : wave % 4) * 32;
     const int my_row = wave_row0 + col;
 
     // Q8 fragment: two k-steps of 64 channels, 32 codes per lane each.  softmax(c*s) with
@@ -187,7 +198,7 @@ next_item:
         const u32x4 b = buffer_load_b128(qrs, off + (MX ? 32 : 16)) ^ qsign;
         qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
-    const float q_scale = MX ? 1.f : p.q_scale[static_cast<int64_t>(bh) * p.nq + mblk];
+    const float q_scale = MX || wblk >= p.nq ? 1.f : p.q_scale[static_cast<int64_t>(bh) * p.nq + wblk];
     const float cq = q_scale * fabsf(p.scale_log2);   // base-2 factor of this block's scores, >= 0
     // MXFP8: the E8M0 byte of each k-step's 32 channels of this lane's query, in bits 0-7
     uint32_t qe[KS];
@@ -627,6 +638,19 @@ hipError_t launch_attn_fwd_fp8(const Fp8AttnParams& p, int d, bool causal, hipSt
     if (nwg == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(nwg));
     const bool mx = p.q_exps != nullptr;
+    // non-causal d128: two query blocks per workgroup when that grid still fills the device
+    if (d == 128 && !causal && MHA_FP8_BLOCKS_PER_WG > 1) {
+        constexpr int R = MHA_FP8_BLOCKS_PER_WG;
+        const int64_t nwg_r = static_cast<int64_t>(p.b) * p.hq * ((p.n_mblocks + R - 1) / R);
+        const auto kernel = mx ? attn_fwd_fp8_kernel<128, false, true, R> : attn_fwd_fp8_kernel<128, false, false, R>;
+        int groups = 0;
+        const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), NTHREADS * R, &groups);
+        if (e != hipSuccess) return e;
+        if (nwg_r >= groups) {
+            hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nwg_r)), dim3(NTHREADS * R), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     auto go = [&](auto d_c) {
         constexpr int DD = decltype(d_c)::value;
         if (mx && causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DD, true, true>), grid, dim3(NTHREADS), 0, stream, p);

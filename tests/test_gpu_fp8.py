@@ -133,6 +133,16 @@ def test_causal_pairs_ragged(shape, d):
     _check_attention(q, k, v, _oracle_mu(k), True, f"causal pairs d{d} {sq}x{sk}")
 
 
+@pytest.mark.parametrize("sq, sk", [(300, 333), (640, 200)])
+def test_two_blocks_per_workgroup(sq, sk):
+    # non-causal d128 grids that still fill the device with two query blocks per workgroup (256
+    # heads) take the packed kernel; an odd block count leaves the last workgroup's second block
+    # empty (no rows to store)
+    q, k, v = _inputs(1, sq, sk, 256, 256, 128, 950 + sq)
+    _check_attention(q, k, v, _oracle_mu(k), False, f"two blocks per workgroup {sq}x{sk}",
+                     heads=[0, 1, 100, 255])
+
+
 def test_no_smoothing():
     q, k, v = _inputs(1, 256, 384, 2, 2, 128, 700, bias_std=0.0)
     _check_attention(q, k, v, None, False, "no smoothing")

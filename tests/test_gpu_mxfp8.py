@@ -89,6 +89,12 @@ def _check(q, k, v, mu, causal, what, heads=None, rows=None):
     assert_fp8_parity(o_g, o_ref, l_g, lse_ref, what)
 
 
+def test_two_blocks_per_workgroup():
+    # the packed non-causal d128 kernel (256 heads, odd block count) with E8M0 exponents
+    q, k, v = _inputs(1, 300, 333, 256, 256, 128, 5300)
+    _check(q, k, v, _oracle_mu(k), False, "mxfp8 two blocks per workgroup", heads=[0, 1, 128, 255])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_gqa(causal, d):

@@ -132,7 +132,7 @@ __host__ __device__ __forceinline__ int split_causal_tiles(int m, int sk) {
 // HPW: query heads per workgroup.  Under GQA the query heads of one kv head read the same K/V
 // tiles; a workgroup of HPW x (BM / 32) waves takes the same BM rows of HPW such heads, so each
 // tile that the DMA brings into LDS serves HPW times the rows (each wave's rows, diagonal and
-// registers stay as with one head).  Dense grids only.
+// registers stay as with one head).  Without windows, sinks or the key split.
 template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT, int HPW = 1>
 // Windows and sinks at d64 run four workgroups per CU (128 VGPRs): a 128-token window gives a
 // workgroup a few tiles, so the grid is bound by latency more than by issue (measured: the
@@ -143,7 +143,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2 * HPW), (EXT && DQK <= 64
     constexpr int RWAVES = BM / 32;                    // one wave per 32 rows of a head
     constexpr int NTHREADS = BM * 2 * HPW;
     constexpr int NWAVES = NTHREADS / 64;
-    static_assert(HPW == 1 || (!VARLEN && !EXT && !SPLIT), "several heads per workgroup on dense grids only");
+    static_assert(HPW == 1 || (!EXT && !SPLIT), "several heads per workgroup without windows, sinks or key split");
     constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
     constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
     constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
@@ -189,7 +189,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2 * HPW), (EXT && DQK <= 64
         // XCDs very different work.  Deal (sequence, kv head) units round-robin instead: XCD x
         // takes units x, x + 8, ... (every sequence, one kv head in eight, with its query heads
         // and blocks kept together); units past the last full round of 8 keep their own ids.
-        const int unit = per_head * p.group;                 // workgroups per (sequence, kv head)
+        const int unit = per_head * (p.group / HPW);         // workgroups per (sequence, kv head)
         const int full = (nwg / unit / 8) * 8 * unit;
         if (pid < full) {
             const int i = pid >> 3;
@@ -1016,20 +1016,24 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
         return hipGetLastError();
     }
     bool paired = CAUSAL && p.n_mblocks > 1;
-    // d128 under GQA: two query heads per workgroup, when the grid still fills the device
-    if constexpr (DQK == 128 && DV == 128 && !VARLEN && MHA_HEADS_PER_WG > 1) {
+    // d128 under GQA: two query heads per workgroup, when the grid still fills the device (packed
+    // sequences pair blocks by the same rule as below)
+    if constexpr (DQK == 128 && DV == 128 && MHA_HEADS_PER_WG > 1) {
         constexpr int H = MHA_HEADS_PER_WG;
         if (p.group % H == 0) {
-            const int64_t per_head = paired ? (p.n_mblocks + 1) / 2 : p.n_mblocks;
-            const int64_t nwg = static_cast<int64_t>(p.b) * (p.hq / H) * per_head;
+            const auto paired_kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, CAUSAL, false, false, H>;
+            const auto plain_kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, false, false, H>;
             int groups = 0;
-            const auto kernel = paired ? attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, CAUSAL, false, false, H>
-                                       : attn_fwd_bf16_kernel<DQK, DV, CAUSAL, false, false, false, false, H>;
-            const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2 * H, &groups);
+            const hipError_t e = resident_groups(reinterpret_cast<const void*>(plain_kernel), BM * 2 * H, &groups);
             if (e != hipSuccess) return e;
+            const int64_t blocks_h = static_cast<int64_t>(p.b) * (p.hq / H) * p.n_mblocks;
+            bool paired_h = paired;
+            if (paired_h && VARLEN) paired_h = blocks_h <= 8 * static_cast<int64_t>(groups);
+            const int64_t nwg = paired_h ? static_cast<int64_t>(p.b) * (p.hq / H) * ((p.n_mblocks + 1) / 2) : blocks_h;
             if (nwg >= groups) {
                 if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-                hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nwg)), dim3(BM * 2 * H), 0, stream, p);
+                hipLaunchKernelGGL(paired_h ? paired_kernel : plain_kernel, dim3(static_cast<unsigned>(nwg)), dim3(BM * 2 * H),
+                                   0, stream, p);
                 return hipGetLastError();
             }
         }

@@ -288,10 +288,7 @@ next_item:
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
                 const uint32_t off = rowoff == kOutOfRange ? kOutOfRange : rowoff + (kk * 16 + half * 8) * 2;
-                u32x4 w = buffer_load_b128(qrs, off);
-                // softmax(c * s) with c < 0 equals softmax(|c| * (-s)): negate Q (exact) and use |c|
-                if (p.scale_log2 < 0.f) w ^= 0x80008000u;
-                qf[kk] = __builtin_bit_cast(bf16x8, w);
+                qf[kk] = __builtin_bit_cast(bf16x8, buffer_load_b128(qrs, off));
             }
         }
         const float c = fmaxf(fabsf(p.scale_log2), kMinScale);   // base-2 score scale, > 0
@@ -710,6 +707,15 @@ next_item:
             issue_k(t0, k_slot(Zero{}));
             issue_v(t0, v_slot(Zero{}));
             issue_k(t0 + 1, k_slot(One{}));
+            // softmax(c * s) with c < 0 equals softmax(|c| * (-s)): negate Q (exact) and use |c|.
+            // The flip needs Q's data, so it stays behind the DMA requests: the K/V round trip
+            // then overlaps Q's instead of starting after it.
+            __builtin_amdgcn_sched_barrier(0);
+            if (p.scale_log2 < 0.f) {
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk)
+                    qf[kk] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[kk]) ^ 0x80008000u);
+            }
             __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_t0 has landed
             __syncthreads();
             f32x16 s0, s1;

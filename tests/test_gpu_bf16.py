@@ -262,6 +262,23 @@ def test_negative_and_zero_scale(dims):
     np.testing.assert_allclose(lse[0, 0].numpy(), np.log(counts), atol=2 ** -8)
 
 
+def test_negative_scale_in_pairs():
+    # The sign flip of a negative scale runs in every block's prologue: both blocks of a causal
+    # pair (d192: 700 rows are 3 blocks of 256, the pair (2, 0) and the middle block 1) and the
+    # two-heads-per-workgroup kernel's pairs (hq 512 over hk 256, 3 blocks of 128).
+    q = workloads.make_random((1, 700, 2, 192), 3400)
+    k = workloads.make_random((1, 700, 2, 192), 3401)
+    v = workloads.make_random((1, 700, 2, 128), 3402)
+    _check_all(q, k, v, True, "d192 scale=-0.2 causal pairs", scale=-0.2)
+    q = workloads.make_random((1, 300, 512, 128), 3403)
+    k = workloads.make_random((1, 300, 256, 128), 3404)
+    v = workloads.make_random((1, 300, 256, 128), 3405)
+    o, lse = _run(q, k, v, True, -0.15)
+    heads = list(range(0, 512, 41)) + [1, 510, 511]
+    o_ref, l_ref = oracle_heads(q, k, v, heads, None, scale=-0.15, causal=True, batch=0)
+    assert_bf16_parity(to_np(o[0][:, heads]), o_ref, lse[0][heads].numpy().astype(np.float64), l_ref,
+                       "two heads per workgroup scale=-0.15 causal pairs")
+
 def _ramp_inputs(dqk, dv, s, step, seed, rising):
     # every query points along channel 0 and key j carries step * j there (reversed when not
     # rising), so each row's scores climb (or fall) steadily along the keys; the other channels

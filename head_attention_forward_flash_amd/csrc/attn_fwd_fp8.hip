@@ -555,12 +555,14 @@ next_item:
             ke[0] = kexp_load(0);
             ke[1] = kexp_load(1);
         }
+        // the first tile's block scales are requested with its K/V, not after the barrier below
+        // (a fence: loads stay behind it), which would add a round trip before the first scores
+        TileScale sc = tile_scale(0);
         issue_k(0, k_slot(Zero{}));
         issue_v(0, v_slot(Zero{}));
         issue_k(1, k_slot(One{}));
         __builtin_amdgcn_s_waitcnt(WAIT_K0);   // this wave's part of K_0 has landed
         __syncthreads();
-        TileScale sc = tile_scale(0);
         f32x16 s0, s1;
         PWords p0, p1;
         KPre pre;

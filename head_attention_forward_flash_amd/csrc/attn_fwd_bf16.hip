@@ -143,7 +143,7 @@ __global__ __launch_bounds__((TileCfg<DQK, DV>::BM * 2 * HPW), (EXT && DQK <= 64
     constexpr int RWAVES = BM / 32;                    // one wave per 32 rows of a head
     constexpr int NTHREADS = BM * 2 * HPW;
     constexpr int NWAVES = NTHREADS / 64;
-    static_assert(HPW == 1 || (!EXT && !SPLIT), "several heads per workgroup without windows, sinks or key split");
+    static_assert(HPW == 1 || !SPLIT, "several heads per workgroup without the key split");
     constexpr int BN = TileCfg<DQK, DV>::BN;           // keys per tile
     constexpr int KROWB = DQK * 2;            // bytes per K row in LDS (16-byte chunks XOR-swizzled)
     constexpr int VROWB = DV * 2;             // bytes per V row in LDS (row-major, swizzled)
@@ -1017,6 +1017,25 @@ hipError_t launch(AttnParams p, hipStream_t stream) {
     }
     if (ext) {
         if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        // sinks (and right windows) under GQA: two query heads per workgroup as below (d64,
+        // d128).  Not with a left window: its blocks see few keys each and are bound by the
+        // latency of their first loads, which more, smaller workgroups per CU hide better (the
+        // 128-key window layer of the GPT-OSS shape: 71.0 -> 75.2 us packed; its full layer
+        // with sinks: 621 -> 600 us)
+        if constexpr ((DQK == 64 || DQK == 128) && DQK == DV && MHA_HEADS_PER_WG > 1) {
+            constexpr int H = MHA_HEADS_PER_WG;
+            if (p.group % H == 0 && p.window_left < 0) {
+                const auto kernel = attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, true, false, H>;
+                int groups = 0;
+                const hipError_t e = resident_groups(reinterpret_cast<const void*>(kernel), BM * 2 * H, &groups);
+                if (e != hipSuccess) return e;
+                const int64_t nwg = static_cast<int64_t>(p.b) * (p.hq / H) * p.n_mblocks;
+                if (nwg >= groups) {
+                    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nwg)), dim3(BM * 2 * H), 0, stream, p);
+                    return hipGetLastError();
+                }
+            }
+        }
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, CAUSAL, VARLEN, false, true, false>),
                            dim3(static_cast<unsigned>(blocks)), dim3(BM * 2), 0, stream, p);
         return hipGetLastError();

@@ -148,3 +148,34 @@ def test_packed_sequences_with_window_and_sinks(dims, causal, left, right):
                                                        sinks=sinks.astype(np.float64))
     assert_bf16_parity(to_np(o.cpu()), o_ref, lse.cpu().numpy().astype(np.float64), l_ref,
                        f"packed window d{dqk} causal={causal} ({left},{right})")
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)], ids=["d64", "d128"])
+@pytest.mark.parametrize("causal,left,right", [(True, -1, -1), (False, -1, 33), (False, -1, -1), (True, 100, -1)])
+def test_two_heads_per_workgroup_window_sinks(dims, causal, left, right):
+    # GQA grids that fill the device (hq 512 over hk 256, 3 blocks of 128 rows) run two query
+    # heads per workgroup with sinks and right windows too: each wave takes its own head's sink
+    # and its own rows' window; both heads of a workgroup (even and odd) are checked, dense and
+    # packed.  (A left window keeps one head per workgroup: the last case.)
+    import head_attention_forward_flash_amd as mha
+    dev = require_gpu()
+    dqk, dv = dims
+    heads = [0, 1, 2, 3, 100, 257, 510, 511]
+    sinks = workloads.make_random((512,), 6700 + dqk, dtype=torch.float32, std=2.0).numpy()
+    q, k, v = _inputs(1, 300, 300, 512, 256, dqk, dv, 6710 + dqk + left)
+    _check(q, k, v, causal, left, right, sinks, f"two heads window d{dqk} causal={causal} ({left},{right})",
+           heads=heads)
+    lens = [200, 333, 90]
+    q = workloads.make_random((sum(lens), 512, dqk), 6720 + dqk)
+    k = workloads.make_random((sum(lens), 256, dqk), 6721 + dqk)
+    v = workloads.make_random((sum(lens), 256, dv), 6722 + dqk)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    o, lse = mha.mha_fwd_bf16_varlen(q.to(dev), k.to(dev), v.to(dev), cu, cu, max(lens), max(lens), causal=causal,
+                                     window_left=left, window_right=right, sinks=torch.from_numpy(sinks).to(dev))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen_window_sink(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                                       cu.cpu().numpy(), cu.cpu().numpy(), scale=dqk ** -0.5,
+                                                       causal=causal, window_left=left, window_right=right,
+                                                       sinks=sinks.astype(np.float64), heads=heads)
+    assert_bf16_parity(to_np(o.cpu())[:, heads], o_ref, lse.cpu().numpy().astype(np.float64)[heads], l_ref,
+                       f"two heads packed window d{dqk} causal={causal} ({left},{right})")

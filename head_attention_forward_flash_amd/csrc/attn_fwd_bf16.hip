@@ -476,16 +476,37 @@ next_item:
             }
             return m;
         };
+        //      With windows or sinks compiled in, the keys the lane's row sees form one interval
+        //      [key_lo, key_lo + key_range]: below sk, up to the diagonal (causal) or the right
+        //      window, from the left window; a row that sees none gets [INT_MAX, INT_MAX], which
+        //      no key reaches.  Score j of block u has key blk*32 + half*4 + c_j (c_j = 8*(j/4) +
+        //      j%4); it is visible iff 0 <= key - key_lo <= key_range, one unsigned compare of
+        //      c_j - a with a = key_lo - blk*32 - half*4 (keys, key_lo and the range all lie in
+        //      [0, 2^31)): three VALU instructions per score instead of about five plus three
+        //      SALU, which pays where windows put an edge in most blocks.  The plain kernels mask
+        //      a block or two per wave and keep the direct test.
+        [[maybe_unused]] int key_lo = 0, key_hi = sk - 1;
+        if constexpr (EXT) {
+            if constexpr (CAUSAL) key_hi = min(key_hi, my_row);
+            if (p.window_left >= 0) key_lo = max(0, my_row - p.window_left);
+            if (!CAUSAL && p.window_right >= 0 && p.window_right < key_hi - my_row) key_hi = my_row + p.window_right;
+            if (key_hi < key_lo) key_lo = key_hi = INT_MAX;
+        }
+        [[maybe_unused]] const uint32_t key_range = static_cast<uint32_t>(key_hi) - static_cast<uint32_t>(key_lo);
         auto mask_block = [&](int u, f32x16& s) __attribute__((always_inline)) {
+            if constexpr (EXT) {
+                const uint32_t a = static_cast<uint32_t>(key_lo) - static_cast<uint32_t>(blk_at(u) * 32 + half * 4);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = blk_at(u) * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                bool out = key >= sk || (CAUSAL && key > my_row);
-                if constexpr (EXT) {
-                    out = out || (p.window_left >= 0 && key < my_row - p.window_left) ||
-                          (!CAUSAL && p.window_right >= 0 && key > my_row + p.window_right);
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t t = static_cast<uint32_t>((j >> 2) * 8 + (j & 3)) - a;
+                    if (t > key_range) s[j] = kNegInf;
                 }
-                if (out) s[j] = kNegInf;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = blk_at(u) * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+                    if (key >= sk || (CAUSAL && key > my_row)) s[j] = kNegInf;
+                }
             }
         };
         // ---- this lane's max over its 16 scores of a block

@@ -31,9 +31,9 @@ def _run(q, k, v, causal, left, right, sinks, scale=None):
     return o.cpu(), lse.cpu()
 
 
-def _check(q, k, v, causal, left, right, sinks, what, rows=None, heads=None):
-    scale = q.shape[3] ** -0.5
-    o, lse = _run(q, k, v, causal, left, right, sinks)
+def _check(q, k, v, causal, left, right, sinks, what, rows=None, heads=None, scale=None):
+    scale = q.shape[3] ** -0.5 if scale is None else scale
+    o, lse = _run(q, k, v, causal, left, right, sinks, scale)
     o_ref, l_ref = oracle.attention_window_sink(q.float().numpy(), k.float().numpy(), v.float().numpy(),
                                                 scale=scale, causal=causal, window_left=left, window_right=right,
                                                 sinks=None if sinks is None else np.asarray(sinks, np.float64),
@@ -179,3 +179,14 @@ def test_two_heads_per_workgroup_window_sinks(dims, causal, left, right):
                                                        sinks=sinks.astype(np.float64), heads=heads)
     assert_bf16_parity(to_np(o.cpu())[:, heads], o_ref, lse.cpu().numpy().astype(np.float64)[heads], l_ref,
                        f"two heads packed window d{dqk} causal={causal} ({left},{right})")
+
+
+@pytest.mark.parametrize("hq,hk", [(4, 2), (512, 256)], ids=["one-head", "two-heads"])
+def test_negative_scale_with_window_and_sinks(hq, hk):
+    # a negative scale flips Q's sign in every block's prologue, in the window/sink kernels too
+    # (hq 512 over hk 256 with sinks and no left window takes the two-heads-per-workgroup kernel)
+    heads = None if hq == 4 else [0, 1, 255, 510, 511]
+    sinks = workloads.make_random((hq,), 6800 + hq, dtype=torch.float32, std=2.0).numpy()
+    q, k, v = _inputs(1, 300, 300, hq, hk, 64, 64, 6810 + hq)
+    _check(q, k, v, True, -1, -1, sinks, f"scale=-0.2 sinks hq={hq}", heads=heads, scale=-0.2)
+    _check(q, k, v, True, 100, -1, sinks, f"scale=-0.2 window sinks hq={hq}", heads=heads, scale=-0.2)

@@ -132,7 +132,8 @@ __host__ __device__ __forceinline__ int split_causal_tiles(int m, int sk) {
 // HPW: query heads per workgroup.  Under GQA the query heads of one kv head read the same K/V
 // tiles; a workgroup of HPW x (BM / 32) waves takes the same BM rows of HPW such heads, so each
 // tile that the DMA brings into LDS serves HPW times the rows (each wave's rows, diagonal and
-// registers stay as with one head).  Without windows, sinks or the key split.
+// registers stay as with one head).  Not with the key split; with windows and sinks only where
+// no left window is set (the launcher decides).
 template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool PAIRED, bool EXT, bool SPLIT, int HPW = 1>
 // Windows and sinks at d64 run four workgroups per CU (128 VGPRs): a 128-token window gives a
 // workgroup a few tiles, so the grid is bound by latency more than by issue (measured: the
